@@ -1,0 +1,428 @@
+"""Pins for the fp64 oracle (CPU only, no GPU).
+
+Each test ties an oracle function to something other than itself: a planted
+input whose answer is a closed form, an exactly rounded sum, an exhaustive
+search, torch's scaled_dot_product_attention, or an invariant the method must
+satisfy.  The sources for what MSA computes are cited in oracle/msa_oracle.c.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_03_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_bits(x):
+    """float array -> bf16 raw bits (inputs here are chosen bf16-exact)."""
+    t = torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+    back = t.float().numpy()
+    assert np.array_equal(back, np.asarray(x, np.float32)), "value not bf16-exact"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_float(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double()
+
+
+def paged(logical, Bk, perm_seed):
+    """Scatter per-sequence logical caches [L_s, H, X] into a permuted page pool.
+
+    Returns (pool [P, H, Bk, X], block_table [B, maxblk]).
+    """
+    nblk = [(x.shape[0] + Bk - 1) // Bk for x in logical]
+    P = sum(nblk)
+    H, X = logical[0].shape[1], logical[0].shape[2]
+    order = np.random.default_rng(perm_seed).permutation(P)
+    pool = np.zeros((P, H, Bk, X), np.float32)
+    bt = np.zeros((len(logical), max(nblk)), np.int32)
+    off = 0
+    for s, x in enumerate(logical):
+        for b in range(nblk[s]):
+            page = order[off + b]
+            bt[s, b] = page
+            chunk = x[b * Bk:(b + 1) * Bk]
+            pool[page, :, :chunk.shape[0], :] = np.transpose(chunk, (1, 0, 2))
+        off += nblk[s]
+    return pool, bt
+
+
+# --------------------------------------------------------------------------
+# positions
+# --------------------------------------------------------------------------
+def test_positions_are_the_last_tokens_of_each_sequence():
+    seq_of, pos_of = oracle.positions([10, 7, 300], [0, 1, 4, 6])
+    assert seq_of.tolist() == [0, 1, 1, 1, 2, 2]
+    assert pos_of.tolist() == [9, 4, 5, 6, 298, 299]
+    with pytest.raises(ValueError):
+        oracle.positions([2], [0, 3])
+
+
+# --------------------------------------------------------------------------
+# index scores
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("H_idx", [1, 3])
+def test_scores_planted_closed_form(H_idx):
+    """k_idx grows linearly with the token position, q_idx is a signed unit
+    vector per group.  A positive q_idx then scores each block by its last
+    causally visible token, a negative one by its first token: closed forms
+    that fail on a wrong causal bound, page mapping, group or index head."""
+    Bk, d, H_kv = 4, 8, 3
+    seq_lens, n_new = [13, 22], [1, 4]
+    logical = []
+    for L in seq_lens:
+        x = np.zeros((L, H_idx, d), np.float32)
+        for j in range(L):
+            for ih in range(H_idx):
+                for dim in range(H_kv):
+                    x[j, ih, dim] = (j + 1) * (dim + 1) * (ih + 1)
+        logical.append(x)
+    pool, bt = paged(logical, Bk, 7)
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    T = int(cu[-1])
+    coef = np.zeros((T, H_kv))
+    q_idx = np.zeros((T, H_kv, d), np.float32)
+    for t in range(T):
+        for g in range(H_kv):
+            c = [1.0, 2.0, -1.0, -2.0][(t + 2 * g) % 4]
+            coef[t, g] = c
+            q_idx[t, g, g] = c
+    seq_of, pos_of = oracle.positions(seq_lens, cu)
+    sc = oracle.index_score(bf16_bits(q_idx), bf16_bits(pool), bt, seq_of, pos_of, Bk)
+    sc = sc.reshape(T, H_kv, -1)
+    for t in range(T):
+        p = int(pos_of[t])
+        for g in range(H_kv):
+            head = (g + 1) if H_idx > 1 else 1
+            for b in range(bt.shape[1]):
+                if b > p // Bk:
+                    assert sc[t, g, b] == -math.inf
+                    continue
+                j = min((b + 1) * Bk - 1, p) if coef[t, g] > 0 else b * Bk
+                want = coef[t, g] * (j + 1) * (g + 1) * head
+                assert sc[t, g, b] == want, (t, g, b)
+
+
+def test_scores_match_exactly_rounded_sums():
+    """Random bf16 data: each fp64 score equals the exactly rounded (fsum)
+    maximum of the visible tokens' dot products to 1e-12 relative."""
+    cfg = gen.MsaConfig("tiny", [300, 129], [1, 3], 8, 2, permute_pages=True, seed=11)
+    x = gen.make_inputs(cfg)
+    qi, kc = gen.bits(x.q_idx), gen.bits(x.kidx_cache)
+    bt = gen.bits(x.block_table)
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    sc = oracle.index_score(qi, kc, bt, seq_of, pos_of, cfg.block_size)
+    qf, kf = bf16_float(qi).numpy(), bf16_float(kc).numpy()
+    Bk = cfg.block_size
+    for row in range(cfg.total_q * cfg.num_kv_heads):
+        t, g = divmod(row, cfg.num_kv_heads)
+        s, p = int(seq_of[t]), int(pos_of[t])
+        for b in range(p // Bk + 1):
+            best = -math.inf
+            for j in range(b * Bk, min((b + 1) * Bk, p + 1)):
+                kv = kf[bt[s, j // Bk], 0, j % Bk]
+                best = max(best, math.fsum(qf[t, g] * kv))
+            assert abs(sc[row, b] - best) <= 1e-12 * max(1.0, abs(best))
+
+
+# --------------------------------------------------------------------------
+# top-k selection
+# --------------------------------------------------------------------------
+def _dominance_ok(S, scores, b_loc, k):
+    """The selection rule stated as a property of the chosen set: the own
+    block is in, the size is min(k, b_loc+1), and every other chosen block
+    beats every unchosen one (higher score, or equal score and lower index)."""
+    n = b_loc + 1
+    if b_loc not in S or len(S) != min(k, n):
+        return False
+    for b in S:
+        if b == b_loc:
+            continue
+        for c in range(n):
+            if c in S:
+                continue
+            if not (scores[b] > scores[c] or (scores[b] == scores[c] and b < c)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_exhaustive_subset_search(seed):
+    rng = np.random.default_rng(seed)
+    k = 4
+    for _ in range(20):
+        n = int(rng.integers(1, 10))
+        b_loc = n - 1
+        scores = rng.integers(-2, 3, size=n).astype(np.float64)  # many ties
+        if rng.random() < 0.3:
+            scores = rng.standard_normal(n)
+        width = n + 2
+        row = np.full(width, -math.inf)
+        row[:n] = scores
+        got = oracle.topk(row[None, :], np.array([b_loc]), k)[0]
+        n_sel = min(k, n)
+        winners = [set(S) for S in itertools.combinations(range(n), n_sel)
+                   if _dominance_ok(set(S), scores, b_loc, k)]
+        assert len(winners) == 1
+        assert got[:n_sel].tolist() == sorted(winners[0])
+        assert (got[n_sel:] == -1).all()
+
+
+def test_topk_special_cases():
+    k = 4
+    # all equal -> lowest indices, plus the own block
+    s = np.zeros((1, 10))
+    assert oracle.topk(s, [9], k)[0].tolist() == [0, 1, 2, 9]
+    # the own block wins even when it scores lowest
+    s = np.array([[5.0, 4.0, 3.0, 2.0, 1.0, -100.0]])
+    assert oracle.topk(s, [5], k)[0].tolist() == [0, 1, 2, 5]
+    # a block after the own block is never eligible
+    s = np.array([[0.0, 0.0, 0.0, 9.0, 9.0]])
+    assert oracle.topk(s, [2], k)[0].tolist() == [0, 1, 2, -1]
+    # -0.0 and +0.0 are equal: the lower index wins
+    s = np.array([[1.0, -0.0, 0.0, -0.0, 0.0, 5.0, 0.0]])
+    assert oracle.topk(s, [6], 3)[0].tolist() == [0, 5, 6]
+    s = np.array([[0.0, 0.0, -0.0, 0.0, 0.0]])
+    assert oracle.topk(s, [4], 3)[0].tolist() == [0, 1, 4]
+
+
+def test_topk_constants_from_the_pages():
+    """Bk = 128 and k = 16 give 2048 tokens per query and group (golden)."""
+    with open(os.path.join(GOLDEN, "msa_constants.json")) as f:
+        c = json.load(f)
+    assert c["block_size"] * c["topk"] == c["tokens_per_query_and_group"] == 2048
+    n = 500
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((5, n))
+    sel = oracle.topk(s, [n - 1] * 5, c["topk"])
+    assert ((sel >= 0).sum(axis=1) == c["topk"]).all()
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _sdpa_reference(q_bits, k_log, v_log, seq_of, pos_of, allowed_fn, G):
+    """torch SDPA in float64 per query token; allowed_fn(t) -> bool mask [L]."""
+    q = bf16_float(q_bits)
+    outs = []
+    for t in range(q.shape[0]):
+        s = int(seq_of[t])
+        kk = bf16_float(k_log[s]).permute(1, 0, 2).repeat_interleave(G, 0)  # [H_q, L, D]
+        vv = bf16_float(v_log[s]).permute(1, 0, 2).repeat_interleave(G, 0)
+        mask = torch.from_numpy(allowed_fn(t))[None, None, :]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[t][:, None, :], kk, vv, attn_mask=mask)
+        outs.append(o[:, 0, :])
+    return torch.stack(outs).numpy()
+
+
+def _attn_case(seq_lens, n_new, H_q, H_kv, D, Bk, seed):
+    rng = np.random.default_rng(seed)
+    r = lambda *sh: bf16_bits(torch.randn(*sh, generator=torch.Generator().manual_seed(
+        int(rng.integers(1 << 30)))).to(torch.bfloat16).float().numpy())
+    k_log = [r(L, H_kv, D) for L in seq_lens]
+    v_log = [r(L, H_kv, D) for L in seq_lens]
+    kf = [bf16_float(x).numpy().astype(np.float32) for x in k_log]
+    vf = [bf16_float(x).numpy().astype(np.float32) for x in v_log]
+    kpool, bt = paged(kf, Bk, seed + 1)
+    vpool, bt2 = paged(vf, Bk, seed + 1)
+    assert (bt == bt2).all()
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    q = r(int(cu[-1]), H_q, D)
+    seq_of, pos_of = oracle.positions(seq_lens, cu)
+    return q, k_log, v_log, bf16_bits(kpool), bf16_bits(vpool), bt, seq_of, pos_of
+
+
+def test_attention_dense_case_equals_sdpa():
+    """All blocks selected: MSA attention is causal softmax attention."""
+    Bk, k, H_q, H_kv, D = 4, 8, 6, 2, 16
+    seq_lens, n_new = [23, 9, 32], [3, 1, 2]
+    q, kl, vl, kp, vp, bt, seq_of, pos_of = _attn_case(seq_lens, n_new, H_q, H_kv, D, Bk, 5)
+    T = q.shape[0]
+    sel = np.full((T, H_kv, k), -1, np.int32)
+    for t in range(T):
+        nb = pos_of[t] // Bk + 1
+        sel[t, :, :nb] = np.arange(nb)
+    out, lse = oracle.attention(q, kp, vp, bt, seq_of, pos_of, sel)
+    ref = _sdpa_reference(q, kl, vl, seq_of, pos_of,
+                          lambda t: np.arange(seq_lens[seq_of[t]]) <= pos_of[t], H_q // H_kv)
+    np.testing.assert_allclose(out.reshape(T, H_q, D), ref, rtol=0, atol=1e-12)
+    # lse against torch.logsumexp of the scaled, masked logits
+    qd = bf16_float(q).numpy()
+    for t in range(T):
+        s = seq_of[t]
+        kk = bf16_float(kl[s]).numpy()[: pos_of[t] + 1]
+        for h in range(H_q):
+            z = kk[:, h // (H_q // H_kv)] @ qd[t, h] / math.sqrt(D)
+            want = torch.logsumexp(torch.from_numpy(z), 0).item()
+            assert abs(lse[t * H_q + h] - want) < 1e-12
+
+
+def test_attention_sparse_case_equals_masked_sdpa():
+    """A hand-chosen selection: attention over exactly the union of the chosen
+    blocks, cut at the query position."""
+    Bk, k, H_q, H_kv, D = 4, 3, 4, 2, 8
+    seq_lens, n_new = [30], [2]
+    q, kl, vl, kp, vp, bt, seq_of, pos_of = _attn_case(seq_lens, n_new, H_q, H_kv, D, Bk, 9)
+    assert pos_of.tolist() == [28, 29]
+    sel = np.array([[[0, 3, 7], [2, 5, 7]], [[1, -1, 7], [6, 7, -1]]], np.int32)
+
+    def allowed(t, g):
+        m = np.zeros(30, bool)
+        for b in sel[t, g]:
+            if b >= 0:
+                m[b * Bk:(b + 1) * Bk] = True
+        m[pos_of[t] + 1:] = False
+        return m
+
+    out, lse = oracle.attention(q, kp, vp, bt, seq_of, pos_of, sel)
+    out = out.reshape(2, H_q, D)
+    G = H_q // H_kv
+    for g in range(H_kv):
+        ref = _sdpa_reference(q, kl, vl, seq_of, pos_of, lambda t: allowed(t, g), G)
+        np.testing.assert_allclose(out[:, g * G:(g + 1) * G], ref[:, g * G:(g + 1) * G],
+                                   rtol=0, atol=1e-12)
+
+
+def test_attention_zero_query_closed_form():
+    """q = 0 makes every logit 0: lse = ln(#attended tokens) and the output is
+    the plain mean of the attended V rows.  Also the duplicate and -1 entries
+    of a selection add nothing."""
+    Bk, k, H_q, H_kv, D = 8, 4, 2, 1, 8
+    seq_lens, n_new = [45], [1]
+    q, kl, vl, kp, vp, bt, seq_of, pos_of = _attn_case(seq_lens, n_new, H_q, H_kv, D, Bk, 2)
+    q[:] = 0
+    p = int(pos_of[0])
+    assert p == 44 and p // Bk == 5
+    sel = np.array([[[1, 3, 5, 3]]], np.int32)
+    out, lse = oracle.attention(q, kp, vp, bt, seq_of, pos_of, sel)
+    n_att = 8 + 8 + (44 - 40 + 1)
+    assert np.allclose(lse, math.log(n_att), atol=1e-14)
+    v = bf16_float(vl[0]).numpy()[:, 0]
+    want = np.concatenate([v[8:16], v[24:32], v[40:45]]).mean(axis=0)
+    np.testing.assert_allclose(out[0], want, atol=1e-14)
+    np.testing.assert_allclose(out[1], want, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# LSE merge
+# --------------------------------------------------------------------------
+def test_lse_merge_of_block_partials_equals_single_softmax():
+    Bk, k, H_q, H_kv, D = 4, 4, 4, 2, 16
+    seq_lens, n_new = [26], [3]
+    q, kl, vl, kp, vp, bt, seq_of, pos_of = _attn_case(seq_lens, n_new, H_q, H_kv, D, Bk, 4)
+    T = q.shape[0]
+    sel = np.array([[[0, 2, 4, 6]] * H_kv, [[1, 3, 5, 6]] * H_kv, [[0, 1, 5, 6]] * H_kv],
+                   np.int32)
+    full_o, full_l = oracle.attention(q, kp, vp, bt, seq_of, pos_of, sel)
+    parts_o, parts_l = [], []
+    for i in range(k):
+        one = np.full_like(sel, -1)
+        one[:, :, 0] = sel[:, :, i]
+        o, l = oracle.attention(q, kp, vp, bt, seq_of, pos_of, one)
+        parts_o.append(o)
+        parts_l.append(l)
+    po = np.stack(parts_o, axis=1)
+    pl = np.stack(parts_l, axis=1)
+    mo, ml = oracle.lse_merge(po, pl)
+    np.testing.assert_allclose(mo, full_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml, full_l, rtol=0, atol=1e-12)
+
+
+def test_lse_merge_closed_forms():
+    o = np.array([[[1.0, 2.0], [3.0, 6.0]]])
+    # equal weights: the mean, and ln 2 more mass
+    mo, ml = oracle.lse_merge(o, np.array([[0.5, 0.5]]))
+    assert np.allclose(mo, [[2.0, 4.0]]) and np.isclose(ml[0], 0.5 + math.log(2))
+    # an empty part (-inf) changes nothing
+    mo, ml = oracle.lse_merge(o, np.array([[1.25, -math.inf]]))
+    assert np.allclose(mo, [[1.0, 2.0]]) and ml[0] == 1.25
+    mo, ml = oracle.lse_merge(o, np.array([[-math.inf, -math.inf]]))
+    assert np.all(mo == 0) and ml[0] == -math.inf
+
+
+# --------------------------------------------------------------------------
+# decode page table: flattening the KV group into the batch
+# --------------------------------------------------------------------------
+def test_page_table_row_length_hand_example():
+    # L = 300, Bk = 128: p = 299, own block 2 holds 44 visible tokens
+    sel = np.array([[[0, 2, -1, -1]]], np.int32)
+    bt = np.array([[7, 3, 9]], np.int32)
+    pt, rl = oracle.page_table(sel, bt, [300], 128)
+    assert pt.tolist() == [[7, 9, -1, -1]] and rl.tolist() == [128 + 44]
+
+
+def test_flattened_paged_attention_equals_per_group_attention():
+    cfg = gen.MsaConfig("tiny_decode", [700, 129, 1000], [1, 1, 1], 12, 3, topk=4,
+                        permute_pages=True, seed=21)
+    x = gen.make_inputs(cfg)
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    bt = gen.bits(x.block_table)
+    sc = oracle.index_score(gen.bits(x.q_idx), gen.bits(x.kidx_cache), bt, seq_of, pos_of, 128)
+    sel = oracle.topk(sc, oracle.b_loc_rows(pos_of, 3, 128), 4).reshape(3, 3, 4)
+    ref_o, ref_l = oracle.attention(gen.bits(x.q), gen.bits(x.k_cache), gen.bits(x.v_cache),
+                                    bt, seq_of, pos_of, sel)
+    pt, rl = oracle.page_table(sel, bt, cfg.seq_lens, 128)
+    o, l = oracle.paged_attention(gen.bits(x.q), gen.bits(x.k_cache), gen.bits(x.v_cache), pt, rl)
+    np.testing.assert_allclose(o.reshape(-1, 128), ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l.reshape(-1), ref_l, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the three whole-method self-checks
+# --------------------------------------------------------------------------
+def _pipeline(cfg, x):
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    bt = gen.bits(x.block_table)
+    sc = oracle.index_score(gen.bits(x.q_idx), gen.bits(x.kidx_cache), bt, seq_of, pos_of,
+                            cfg.block_size)
+    H_kv = cfg.num_kv_heads
+    sel = oracle.topk(sc, oracle.b_loc_rows(pos_of, H_kv, cfg.block_size), cfg.topk)
+    sel = sel.reshape(cfg.total_q, H_kv, cfg.topk)
+    o, l = oracle.attention(gen.bits(x.q), gen.bits(x.k_cache), gen.bits(x.v_cache), bt,
+                            seq_of, pos_of, sel)
+    return seq_of, pos_of, sel, o, l
+
+
+def test_self_check_dense_when_budget_covers_the_context():
+    """k*Bk >= L: the method is dense causal attention (SDPA, float64)."""
+    cfg = gen.MsaConfig("dense", [2048, 1500], [2, 3], 8, 2, permute_pages=True, seed=8)
+    x = gen.make_inputs(cfg)
+    seq_of, pos_of, sel, o, l = _pipeline(cfg, x)
+    q = bf16_float(gen.bits(x.q))
+    for t in range(cfg.total_q):
+        s, p = int(seq_of[t]), int(pos_of[t])
+        nb = cfg.blocks_per_seq[s]
+        pages = gen.bits(x.block_table)[s, :nb]
+        kk = bf16_float(gen.bits(x.k_cache)[pages]).permute(1, 0, 2, 3).reshape(2, -1, 128)
+        vv = bf16_float(gen.bits(x.v_cache)[pages]).permute(1, 0, 2, 3).reshape(2, -1, 128)
+        kk, vv = kk[:, : p + 1].repeat_interleave(4, 0), vv[:, : p + 1].repeat_interleave(4, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[t][:, None], kk, vv)[:, 0]
+        np.testing.assert_allclose(o.reshape(cfg.total_q, 8, 128)[t], ref.numpy(), atol=1e-12)
+
+
+def test_self_check_budget_invariant():
+    """At most k*Bk tokens per query and group, own block always chosen, no
+    block after it: checked through lse with q = 0 (lse = ln #tokens)."""
+    cfg = gen.MsaConfig("budget", [5000, 3000, 2600], [1, 4, 1], 8, 2, permute_pages=True,
+                        seed=9)
+    x = gen.make_inputs(cfg)
+    x.q.zero_()
+    seq_of, pos_of, sel, o, l = _pipeline(cfg, x)
+    Bk = cfg.block_size
+    for t in range(cfg.total_q):
+        b_loc = pos_of[t] // Bk
+        for g in range(cfg.num_kv_heads):
+            chosen = sel[t, g][sel[t, g] >= 0]
+            assert b_loc in chosen and chosen.max() == b_loc
+            assert len(chosen) == min(cfg.topk, b_loc + 1)
+    n_att = np.exp(l)
+    assert (np.round(n_att) <= cfg.topk * Bk).all()
+    assert np.allclose(n_att, np.round(n_att), atol=1e-8)
