@@ -1,0 +1,211 @@
+"""ctypes binding of libmsa.so (include/msa.h).
+
+Argument marshalling only: every function checks the tensors it is given
+(device, dtype, contiguity, shape), packs ``msa_dims_t`` and calls the C entry
+point of the same name on the current HIP stream.  All arithmetic runs in the
+library's HIP kernels; there is no CPU fallback, and loading fails loudly when
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_SUCCESS = 0
+MSA_ERROR_INVALID_VALUE = 1
+MSA_ERROR_NOT_SUPPORTED = 2
+MSA_ERROR_WORKSPACE = 3
+MSA_ERROR_LAUNCH = 4
+
+EXPORTED = (
+    "msa_index_score", "msa_topk_blocks", "msa_build_page_table", "msa_sparse_attn_decode",
+    "msa_sparse_attn_prefill", "msa_decode_workspace_size", "msa_prefill_workspace_size",
+    "msa_status_string", "msa_abi_version",
+)
+
+
+class msa_dims_t(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("num_idx_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python block_sparse_attention_03_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(msa_dims_t)
+        L.msa_index_score.argtypes = [D, I32, P, P, P, P, P, P, P]
+        L.msa_topk_blocks.argtypes = [D, I32, P, P, P, P, P]
+        L.msa_build_page_table.argtypes = [D, P, P, P, P, P, P]
+        L.msa_sparse_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
+        L.msa_sparse_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
+                  "msa_sparse_attn_decode", "msa_sparse_attn_prefill"):
+            getattr(L, f).restype = ctypes.c_int
+        L.msa_decode_workspace_size.argtypes = [D]
+        L.msa_decode_workspace_size.restype = SZ
+        L.msa_prefill_workspace_size.argtypes = [D, I32]
+        L.msa_prefill_workspace_size.restype = SZ
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().msa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().msa_abi_version())
+
+
+def make_dims(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, num_pages,
+              num_idx_heads=1, head_dim=128, idx_dim=64, block_size=128, topk=16,
+              softmax_scale=0.0) -> msa_dims_t:
+    return msa_dims_t(num_seqs, num_q_heads, num_kv_heads, num_idx_heads, head_dim, idx_dim,
+                      block_size, topk, max_blocks_per_seq, num_pages, softmax_scale)
+
+
+def dims_for(cfg) -> msa_dims_t:
+    """msa_dims_t of an inputs.MsaConfig."""
+    return make_dims(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.max_blocks,
+                     cfg.num_pages, cfg.num_idx_heads, cfg.head_dim, cfg.idx_dim,
+                     cfg.block_size, cfg.topk)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, where: str):
+    if status != MSA_SUCCESS:
+        raise MsaError(status, where)
+
+
+BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
+
+
+def msa_index_score(dims, total_q, q_idx, kidx_cache, block_table, seq_lens, cu_q, scores,
+                    stream=None):
+    d = dims
+    H, B, W = d.num_kv_heads, d.num_seqs, d.max_blocks_per_seq
+    args = (_ptr(q_idx, BF16, "q_idx", (total_q, H, d.idx_dim)),
+            _ptr(kidx_cache, BF16, "kidx_cache", (d.num_pages, d.num_idx_heads, d.block_size, d.idx_dim)),
+            _ptr(block_table, I32, "block_table", (B, W)), _ptr(seq_lens, I32, "seq_lens", (B,)),
+            _ptr(cu_q, I32, "cu_q", (B + 1,)), _ptr(scores, F32, "scores", (total_q, H, W)))
+    _check(lib().msa_index_score(ctypes.byref(d), total_q, *args, _stream(stream)), "msa_index_score")
+
+
+def msa_topk_blocks(dims, total_q, scores, seq_lens, cu_q, sel, stream=None):
+    d = dims
+    H, B = d.num_kv_heads, d.num_seqs
+    args = (_ptr(scores, F32, "scores", (total_q, H, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
+            _ptr(sel, I32, "sel", (total_q, H, d.topk)))
+    _check(lib().msa_topk_blocks(ctypes.byref(d), total_q, *args, _stream(stream)), "msa_topk_blocks")
+
+
+def msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens, stream=None):
+    d = dims
+    B, H = d.num_seqs, d.num_kv_heads
+    args = (_ptr(sel, I32, "sel", (B, H, d.topk)),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)),
+            _ptr(page_table, I32, "page_table", (B * H, d.topk)),
+            _ptr(row_lens, I32, "row_lens", (B * H,)))
+    _check(lib().msa_build_page_table(ctypes.byref(d), *args, _stream(stream)),
+           "msa_build_page_table")
+
+
+def msa_decode_workspace_size(dims) -> int:
+    return int(lib().msa_decode_workspace_size(ctypes.byref(dims)))
+
+
+def msa_prefill_workspace_size(dims, total_q) -> int:
+    return int(lib().msa_prefill_workspace_size(ctypes.byref(dims), total_q))
+
+
+def msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out, lse, workspace,
+                           stream=None):
+    d = dims
+    B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    args = (_ptr(q, BF16, "q", (B, Hq, d.head_dim)), _ptr(k_cache, BF16, "k_cache", cache),
+            _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(page_table, I32, "page_table", (B * H, d.topk)),
+            _ptr(row_lens, I32, "row_lens", (B * H,)),
+            _ptr(out, BF16, "out", (B, Hq, d.head_dim)),
+            _ptr(lse, F32, "lse", (B, Hq)) if lse is not None else None,
+            _ptr(workspace, torch.uint8, "workspace"))
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().msa_sparse_attn_decode(ctypes.byref(d), *args, nbytes, _stream(stream)),
+           "msa_sparse_attn_decode")
+
+
+def msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel,
+                            out, lse, workspace, stream=None):
+    d = dims
+    B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    args = (_ptr(q, BF16, "q", (total_q, Hq, d.head_dim)), _ptr(k_cache, BF16, "k_cache", cache),
+            _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
+            _ptr(sel, I32, "sel", (total_q, H, d.topk)),
+            _ptr(out, BF16, "out", (total_q, Hq, d.head_dim)),
+            _ptr(lse, F32, "lse", (total_q, Hq)) if lse is not None else None,
+            _ptr(workspace, torch.uint8, "workspace"))
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(lib().msa_sparse_attn_prefill(ctypes.byref(d), total_q, *args, nbytes, _stream(stream)),
+           "msa_sparse_attn_prefill")

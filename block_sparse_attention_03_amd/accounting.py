@@ -1,0 +1,89 @@
+"""Algorithmic work of one MSA layer-step: bytes and flops the method must move.
+
+Counts cover only what the method has to touch -- index keys of every valid
+context token, K and V of the attended tokens, the small per-query vectors --
+and never the dense work that MSA avoids, nor padding or re-reads.  They are
+the numerators of the roofline fractions bench.py reports.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _attended(cfg):
+    """Per (query token) list of (position p, attended tokens per group).
+
+    With top-k over blocks 0..b_loc, a query attends min(k, b_loc+1) blocks:
+    all but its own are full, its own holds p - Bk*b_loc + 1 visible tokens.
+    """
+    Bk, k = cfg.block_size, cfg.topk
+    out = []
+    for L, n in zip(cfg.seq_lens, cfg.n_new):
+        for i in range(n):
+            p = L - n + i
+            b_loc = p // Bk
+            n_sel = min(k, b_loc + 1)
+            out.append((p, (n_sel - 1) * Bk + (p - Bk * b_loc + 1)))
+    return out
+
+
+def score_bytes(cfg) -> int:
+    """Index scoring: every visible token's index key once per index head, the
+    index queries, and the eligible block scores written (fp32)."""
+    kidx = sum(cfg.seq_lens) * cfg.num_idx_heads * cfg.idx_dim * 2
+    qidx = cfg.total_q * cfg.num_kv_heads * cfg.idx_dim * 2
+    sc = sum((p // cfg.block_size + 1) for p, _ in _attended(cfg)) * cfg.num_kv_heads * 4
+    return kidx + qidx + sc
+
+
+def score_flops(cfg) -> int:
+    """2*d*H_kv flops per (query, visible context token)."""
+    return sum(2 * cfg.idx_dim * cfg.num_kv_heads * (p + 1) for p, _ in _attended(cfg))
+
+
+def decode_attn_bytes(cfg) -> int:
+    """K and V of the attended tokens of every (sequence, group) row, q read,
+    out written (bf16) and lse written (fp32)."""
+    D = cfg.head_dim
+    kv = sum(n_att for _, n_att in _attended(cfg)) * cfg.num_kv_heads * 2 * D * 2
+    qo = cfg.total_q * cfg.num_q_heads * (2 * D * 2 + 4)
+    return kv + qo
+
+
+def attn_flops(cfg) -> int:
+    """4*D flops per (query, head, attended token): q.k and p*v."""
+    return sum(4 * cfg.head_dim * cfg.num_q_heads * n_att for _, n_att in _attended(cfg))
+
+
+def prefill_attn_bytes(cfg) -> int:
+    """KV-block-major prefill: each selected (sequence, group, block) K and V
+    once, q read once per (query, head, slot), out + lse written, and the
+    partial outputs (bf16) and LSEs (fp32) written and read back once."""
+    D, Bk = cfg.head_dim, cfg.block_size
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    blocks = 0
+    for L, n in zip(cfg.seq_lens, cfg.n_new):
+        if n:
+            blocks += (L - 1) // Bk + 1  # upper bound: every block is selected by someone
+    kv = blocks * cfg.num_kv_heads * 2 * Bk * D * 2
+    slots = sum(min(cfg.topk, p // Bk + 1) for p, _ in _attended(cfg)) * cfg.num_kv_heads * G
+    q = slots * D * 2
+    partial = slots * (D * 2 + 4) * 2
+    out = cfg.total_q * cfg.num_q_heads * (D * 2 + 4)
+    return kv + q + partial + out
+
+
+def dense_over_msa_flops(L: int, num_q_heads: int, num_idx_q_heads: int, head_dim: int = 128,
+                         idx_dim: int = 64, budget: int = 2048) -> float:
+    """Attention flops per token of dense GQA over those of MSA at context L.
+
+    Dense: 4*D*H_q*L.  MSA: 4*D*H_q*budget (attention over the selected
+    tokens) + 2*d*H_idxq*L (index scoring over the whole context).
+    """
+    dense = 4 * head_dim * num_q_heads * L
+    msa = 4 * head_dim * num_q_heads * min(budget, L) + 2 * idx_dim * num_idx_q_heads * L
+    return dense / msa
+
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, published

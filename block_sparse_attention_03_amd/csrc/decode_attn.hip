@@ -1,0 +1,245 @@
+// decode_attn.hip -- MSA sparse decode attention over the flattened page table.
+//
+// What it computes (aivizor serving-report news item, paragraph on MSA with
+// paged attention): the KV-group dimension is flattened into the batch, so
+// row r = s*H_kv + g is an ordinary paged sequence of row_lens[r] tokens whose
+// pages are page_table[r][0..]; its G = H_q/H_kv query heads attend it with
+// softmax(scale * q K^T) V.
+//
+// Mapping.  One workgroup (4 wavefronts) per (row, page): the page's K and V
+// (2 x 32 KB) are read from HBM exactly once, and the row's G query heads are
+// packed as the 16 columns of 16x16x32 bf16 matrix-core tiles, so one page
+// load serves the whole GQA group.  Wavefront w scores tokens 32w..32w+31
+// (S^T = K Q^T, fp32 accumulate); the page's per-head max and sum are
+// combined through LDS; P is rounded to bf16 and shared through LDS; then
+// wavefront w forms dims 32w..32w+31 of O^T = V^T P^T.  V is written to LDS
+// transposed (two tokens per 32-bit word) so the reduction index (tokens) is
+// contiguous for the matrix core.  Each page leaves a normalised partial
+// output and its log-sum-exp in the workspace; a second kernel merges a row's
+// pages with the Log-Sum-Exp rule (aivizor, KV-Block-Major paragraph).
+#include "msa_common.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kVtStride = kBlock + 8;    // bf16 per transposed-V row (dims x tokens)
+constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecodeWs {
+    float* o;    // [R, k, G, 128] normalised partial outputs
+    float* lse;  // [R, k, G]
+};
+
+__device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
+    DecodeWs w;
+    w.o = static_cast<float*>(ws);
+    w.lse = w.o + (size_t)R * kTopK * G * kHeadDim;
+    return w;
+}
+
+__global__ __launch_bounds__(kDecThreads)
+void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
+                        const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                        const uint16_t* __restrict__ v_cache,
+                        const int32_t* __restrict__ page_table,  // [R, k]
+                        const int32_t* __restrict__ row_lens,    // [R]
+                        void* __restrict__ ws, int Hq, int Hkv, int R, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+    __shared__ __attribute__((aligned(16))) uint16_t pl[kMaxGroup * kPStride];
+    __shared__ float red_max[4][kMaxGroup];
+    __shared__ float red_sum[4][kMaxGroup];
+
+    const int slot = blockIdx.x;
+    const int r = blockIdx.y;
+    const int n_tok = row_lens[r];
+    if (slot * kBlock >= n_tok) return;  // page not used by this row (uniform)
+    const int nv = min(kBlock, n_tok - slot * kBlock);
+    const int G = Hq / Hkv;
+    const int s = r / Hkv;
+    const int g = r % Hkv;
+    const int page = page_table[(size_t)r * kTopK + slot];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    const uint16_t* kp = k_cache + page_off;
+    const uint16_t* vp = v_cache + page_off;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int n = lane % 16;   // head column (B / result) or row of A
+    const int kg = lane / 16;  // lane group
+
+    // V -> LDS, transposed: thread takes token pair tp and 8 dims; tokens at or
+    // past nv are zero so that P = 0 there never meets a non-finite V.
+    {
+        const int tp = tid % 64;
+        u32x4 v0[4], v1[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int d0 = (tid / 64 + 4 * it) * 8;
+            const int t0 = 2 * tp, t1 = 2 * tp + 1;
+            v0[it] = (t0 < nv) ? ld16(vp + t0 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+            v1[it] = (t1 < nv) ? ld16(vp + t1 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        }
+        // K operands for this wave's 32 tokens (rows 32w + 16j + n, dims 32i + 8kg)
+        bf16x8 ka[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ka[j][i] = as_bf16x8(ld16(kp + (32 * wave + 16 * j + n) * kHeadDim + 32 * i + 8 * kg));
+        // Q operands: head n of this group, zero beyond G
+        bf16x8 qb[4];
+        const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
+
+        uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int d0 = (tid / 64 + 4 * it) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (v0[it][e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+                const uint32_t hi = (v1[it][e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+                vt32[((d0 + e) * kVtStride) / 2 + tp] = lo | (hi << 16);
+            }
+        }
+
+        // S^T = K Q^T for tokens 32w + 16j + 4kg + rr, head n
+        f32x4 sacc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[j] = mfma16(ka[j][i], qb[i], sacc[j]);
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int tok = 32 * wave + 16 * j + 4 * kg + rr;
+                if (tok >= nv) sacc[j][rr] = -__builtin_inff();
+                mx = fmaxf(mx, sacc[j][rr]);
+            }
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);
+        if (kg == 0) red_max[wave][n] = mx;
+        __syncthreads();
+        const float m = fmaxf(fmaxf(red_max[0][n], red_max[1][n]), fmaxf(red_max[2][n], red_max[3][n]));
+        // P = exp(scale * (s - m)) rounded to bf16; the sum uses the rounded values
+        float sum = 0.f;
+        uint16_t pb[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float pv = __builtin_amdgcn_exp2f((sacc[j][rr] - m) * scale_log2);
+                pb[j][rr] = f32_to_bf16(pv);
+                sum += bf16_to_f32(pb[j][rr]);
+            }
+        sum += __shfl_xor(sum, 16, kWave);
+        sum += __shfl_xor(sum, 32, kWave);
+        if (kg == 0) red_sum[wave][n] = sum;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int tok = 32 * wave + 16 * j + 4 * kg;
+            u32x2 w2 = {static_cast<uint32_t>(pb[j][0]) | (static_cast<uint32_t>(pb[j][1]) << 16),
+                        static_cast<uint32_t>(pb[j][2]) | (static_cast<uint32_t>(pb[j][3]) << 16)};
+            *reinterpret_cast<u32x2*>(pl + n * kPStride + tok) = w2;
+        }
+        __syncthreads();
+
+        // O^T = V^T P^T for dims 32w .. 32w+31; k-step ks covers tokens 32ks..32ks+31,
+        // lane group kg taking tokens 32ks + 4kg + 0..3 and 32ks + 16 + 4kg + 0..3.
+        f32x4 oacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ta = 32 * ks + 4 * kg;
+            const u32x2 p0 = *reinterpret_cast<const u32x2*>(pl + n * kPStride + ta);
+            const u32x2 p1 = *reinterpret_cast<const u32x2*>(pl + n * kPStride + ta + 16);
+            const bf16x8 pbv = as_bf16x8(u32x4{p0[0], p0[1], p1[0], p1[1]});
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int dim = 32 * wave + 16 * mt + n;
+                const u32x2 v0a = *reinterpret_cast<const u32x2*>(vt + dim * kVtStride + ta);
+                const u32x2 v1a = *reinterpret_cast<const u32x2*>(vt + dim * kVtStride + ta + 16);
+                oacc[mt] = mfma16(as_bf16x8(u32x4{v0a[0], v0a[1], v1a[0], v1a[1]}), pbv, oacc[mt]);
+            }
+        }
+        const float l = red_sum[0][n] + red_sum[1][n] + red_sum[2][n] + red_sum[3][n];
+        if (n < G) {
+            DecodeWs w = decode_ws(ws, R, G);
+            const float inv = 1.0f / l;
+            float* orow = w.o + (((size_t)r * kTopK + slot) * G + n) * kHeadDim;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int d = 32 * wave + 16 * mt + 4 * kg;
+                f32x4 o = oacc[mt] * inv;
+                *reinterpret_cast<f32x4*>(orow + d) = o;
+            }
+            if (wave == 0 && kg == 0)
+                w.lse[((size_t)r * kTopK + slot) * G + n] = m * scale_log2 * kLn2 + __logf(l);
+        }
+    }
+}
+
+// One thread per (row, head, dim): Log-Sum-Exp merge of the row's pages.
+__global__ __launch_bounds__(kHeadDim)
+void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __restrict__ ws,
+                         uint16_t* __restrict__ out, float* __restrict__ lse_out, int Hq,
+                         int Hkv, int R) {
+    const int rn = blockIdx.x;  // r * G + n
+    const int G = Hq / Hkv;
+    const int r = rn / G;
+    const int n = rn % G;
+    const int d = threadIdx.x;
+    const int npages = min(kTopK, ceil_div(row_lens[r], kBlock));
+    DecodeWs w = decode_ws(const_cast<void*>(ws), R, G);
+    const float* lp = w.lse + (size_t)r * kTopK * G + n;
+    float mx = -__builtin_inff();
+    for (int i = 0; i < npages; ++i) mx = fmaxf(mx, lp[i * G]);
+    float den = 0.f, acc = 0.f;
+    for (int i = 0; i < npages; ++i) {
+        const float wi = __expf(lp[i * G] - mx);
+        den += wi;
+        acc += wi * w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d];
+    }
+    const int s = r / Hkv;
+    const int h = (r % Hkv) * G + n;
+    out[((size_t)s * Hq + h) * kHeadDim + d] = f32_to_bf16(acc / den);
+    if (lse_out && d == 0) lse_out[(size_t)s * Hq + h] = mx + __logf(den);
+}
+
+}  // namespace
+}  // namespace msa
+
+size_t msa_decode_ws_bytes(const MsaShape& s) {
+    using namespace msa;
+    const size_t R = (size_t)s.B * s.Hkv;
+    const size_t G = (size_t)(s.Hq / s.Hkv);
+    const size_t bytes = R * kTopK * G * (kHeadDim + 1) * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+hipError_t msa_launch_decode(const MsaShape& s, const uint16_t* q, const uint16_t* k_cache,
+                             const uint16_t* v_cache, const int32_t* page_table,
+                             const int32_t* row_lens, uint16_t* out, float* lse, void* ws,
+                             hipStream_t st) {
+    using namespace msa;
+    const int R = s.B * s.Hkv;
+    if (R == 0) return hipSuccess;
+    const int G = s.Hq / s.Hkv;
+    const float scale_log2 = s.scale * kLog2e;
+    hipLaunchKernelGGL(decode_page_kernel, dim3(kTopK, R), dim3(kDecThreads), 0, st, q, k_cache,
+                       v_cache, page_table, row_lens, ws, s.Hq, s.Hkv, R, scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(R * G), dim3(kHeadDim), 0, st, row_lens, ws, out,
+                       lse, s.Hq, s.Hkv, R);
+    return hipGetLastError();
+}

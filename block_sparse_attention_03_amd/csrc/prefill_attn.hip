@@ -1,0 +1,368 @@
+// prefill_attn.hip -- MSA sparse prefill attention, KV-block-major.
+//
+// What it computes (aivizor serving-report news item, KV-Block-Major
+// paragraph; mechatronicstore "MoE de 428B" page, section on what makes M3
+// different): the outer loop runs over KV blocks, each read from HBM once and
+// contiguously; the inner loop runs over the queries that selected the block,
+// producing partial outputs; a final Log-Sum-Exp reduction recomposes each
+// query's result.  The result equals softmax attention over the union of the
+// query's selected blocks, cut at its position.
+//
+// Steps (all on the caller's stream):
+//   1. inverse map: histogram of (sequence, group, block) buckets over the
+//      selection, exclusive scan, scatter of (query, slot) entries;
+//   2. block-major attention: one workgroup per bucket stages the block's K
+//      (row-major) and V (transposed) in LDS once, then its wavefronts sweep
+//      the bucket's (query, head) rows 32 at a time with 32x32x16 bf16 matrix
+//      cores: S^T = K Q^T, row softmax in registers, P rounded to bf16 and
+//      fed straight from the S^T accumulators as the B operand of
+//      O^T = V^T P^T.  Each (query, head, slot) gets a normalised bf16 partial
+//      output and an fp32 log-sum-exp;
+//   3. merge: per (query, head), the partials of its selected slots combine in
+//      slot order (deterministic; no float atomics).
+#include "msa_common.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kPfThreads = 256;
+constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS
+constexpr int kVtStride = kBlock + 8;    // bf16 per transposed-V row in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct PrefillWs {
+    int32_t* counts;   // [NB]
+    int32_t* offsets;  // [NB + 1]
+    int32_t* cursor;   // [NB]
+    int32_t* entries;  // [total_q * Hkv * k]: query << 4 | slot
+    uint16_t* part_o;  // [total_q, Hq, k, 128] bf16
+    float* part_lse;   // [total_q, Hq, k]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+__host__ __device__ inline PrefillWs prefill_ws(void* base, int NB, int total_q, int Hq, int Hkv) {
+    char* p = static_cast<char*>(base);
+    PrefillWs w;
+    w.counts = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)NB * 4);
+    w.offsets = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)(NB + 1) * 4);
+    w.cursor = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)NB * 4);
+    w.entries = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)total_q * Hkv * kTopK * 4);
+    w.part_o = reinterpret_cast<uint16_t*>(p);
+    p += align256((size_t)total_q * Hq * kTopK * kHeadDim * 2);
+    w.part_lse = reinterpret_cast<float*>(p);
+    p += align256((size_t)total_q * Hq * kTopK * 4);
+    return w;
+}
+
+__host__ __device__ inline size_t prefill_ws_size(int NB, int total_q, int Hq, int Hkv) {
+    PrefillWs w = prefill_ws(nullptr, NB, total_q, Hq, Hkv);
+    return reinterpret_cast<size_t>(w.part_lse) + align256((size_t)total_q * Hq * kTopK * 4);
+}
+
+__device__ __forceinline__ int seq_of_token(const int32_t* cu_q, int B, int t) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ void zero_kernel(int32_t* a, int na, int32_t* b, int nb) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na || i < nb; i += gridDim.x * blockDim.x) {
+        if (i < na) a[i] = 0;
+        if (i < nb) b[i] = 0;
+    }
+}
+
+__global__ void histogram_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
+                                 int32_t* __restrict__ counts, int B, int Hkv, int maxblk, int n) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int b = sel[idx];
+    if (b < 0) return;
+    const int t = idx / (Hkv * kTopK);
+    const int g = (idx / kTopK) % Hkv;
+    const int s = seq_of_token(cu_q, B, t);
+    atomicAdd(&counts[((size_t)s * Hkv + g) * maxblk + b], 1);
+}
+
+// Exclusive scan of counts[0..n) into offsets[0..n], one workgroup.
+__global__ __launch_bounds__(1024)
+void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int n) {
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    const int per = ceil_div(n, 1024);
+    const int a = min(n, tid * per), e = min(n, a + per);
+    int sum = 0;
+    for (int i = a; i < e; ++i) sum += counts[i];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = (tid >= off) ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;  // exclusive prefix of this thread's chunk
+    for (int i = a; i < e; ++i) {
+        offsets[i] = run;
+        run += counts[i];
+    }
+    if (tid == 1023) offsets[n] = part[1023];
+}
+
+__global__ void scatter_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
+                               const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                               int32_t* __restrict__ entries, int B, int Hkv, int maxblk, int n) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int b = sel[idx];
+    if (b < 0) return;
+    const int t = idx / (Hkv * kTopK);
+    const int g = (idx / kTopK) % Hkv;
+    const int slot = idx % kTopK;
+    const int s = seq_of_token(cu_q, B, t);
+    const size_t bk = ((size_t)s * Hkv + g) * maxblk + b;
+    const int pos = offsets[bk] + atomicAdd(&cursor[bk], 1);
+    entries[pos] = (t << 4) | slot;
+}
+
+__global__ __launch_bounds__(kPfThreads)
+void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
+                        const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                        const uint16_t* __restrict__ v_cache,
+                        const int32_t* __restrict__ block_table,
+                        const int32_t* __restrict__ seq_lens,
+                        const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
+                        int maxblk, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kBlock * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+
+    const int bk = blockIdx.x;
+    const int cnt = w.counts[bk];
+    if (cnt == 0) return;
+    const int base = w.offsets[bk];
+    const int b = bk % maxblk;
+    const int g = (bk / maxblk) % Hkv;
+    const int s = bk / (maxblk * Hkv);
+    const int G = Hq / Hkv;
+    const int L = seq_lens[s];
+    const int nq = cu_q[s + 1] - cu_q[s];
+    const int pos0 = L - nq - cu_q[s];  // p = pos0 + t
+    const int nv = min(kBlock, L - b * kBlock);
+    const int page = block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    const uint16_t* kp = k_cache + page_off;
+    const uint16_t* vp = v_cache + page_off;
+    const int tid = threadIdx.x;
+
+    // Stage the block once: K row-major, V transposed (dims x tokens); tokens
+    // past the sequence end are zero.
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int c = tid + kPfThreads * it;
+        const int tok = c / 16, d0 = (c % 16) * 8;
+        const u32x4 v = (tok < nv) ? ld16(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(ks + tok * kKStride + d0) = v;
+    }
+    {
+        const int tp = tid % 64;
+        uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int d0 = (tid / 64 + 4 * it) * 8;
+            const int t0 = 2 * tp, t1 = 2 * tp + 1;
+            const u32x4 v0 = (t0 < nv) ? ld16(vp + t0 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 v1 = (t1 < nv) ? ld16(vp + t1 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (v0[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+                const uint32_t hi = (v1[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+                vt32[((d0 + e) * kVtStride) / 2 + tp] = lo | (hi << 16);
+            }
+        }
+    }
+    __syncthreads();
+
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int n = lane % 32;   // result column = row of this lane
+    const int h = lane / 32;   // lane half
+    const int nrows = cnt * G;
+    const int tok0 = b * kBlock;
+
+    for (int tile = wave; tile * 32 < nrows; tile += kPfThreads / kWave) {
+        const int rho = tile * 32 + n;
+        const bool row_ok = rho < nrows;
+        const int e_idx = row_ok ? rho / G : 0;
+        const int rr_head = row_ok ? rho % G : 0;
+        const int entry = w.entries[base + e_idx];
+        const int t = entry >> 4;
+        const int slot = entry & 15;
+        const int head = g * G + rr_head;
+        const int p = pos0 + t;
+
+        // Q^T operand: k-step i of lane half h takes dims 64h + 8i .. +7
+        bf16x8 qb[8];
+        const uint16_t* qrow = q + ((size_t)t * Hq + head) * kHeadDim + 64 * h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            qb[i] = as_bf16x8(row_ok ? ld16(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u});
+
+        // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
+        // token 32mt + 8(v/4) + 4h + v%4 of row n.
+        f32x16 sacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            sacc[mt] = f32x16{};
+            const uint16_t* krow = ks + (32 * mt + n) * kKStride + 64 * h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sacc[mt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * i)), qb[i],
+                                  sacc[mt]);
+        }
+        // causal cut inside the query's own block
+        const int lim = p - tok0;  // token index (within block) must be <= lim
+        if (lim < kBlock - 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tk = 32 * mt + 8 * (v / 4) + 4 * h + (v % 4);
+                    if (tk > lim) sacc[mt][v] = -__builtin_inff();
+                }
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[mt][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+
+        // P (bf16) as B operands of O^T = V^T P^T; k-step i covers tokens
+        // 16i..16i+15 = accumulator values 8(i%2)..8(i%2)+7 of tile i/2.
+        bf16x8 pb[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float pv = __builtin_amdgcn_exp2f((sacc[i / 2][8 * (i % 2) + e2] - mx) * scale_log2);
+                const __bf16 pbf = static_cast<__bf16>(pv);
+                pb[i][e2] = pbf;
+                sum += static_cast<float>(pbf);
+            }
+        }
+        sum += __shfl_xor(sum, 32, kWave);
+
+        f32x16 oacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            oacc[mt] = f32x16{};
+            const uint16_t* vrow = vt + (32 * mt + n) * kVtStride + 4 * h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 16 * i);
+                const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 * i + 8);
+                oacc[mt] = mfma32(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb[i], oacc[mt]);
+            }
+        }
+        if (row_ok) {
+            const float inv = 1.0f / sum;
+            uint16_t* orow = w.part_o + (((size_t)t * Hq + head) * kTopK + slot) * kHeadDim;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int d = 32 * mt + 8 * qd + 4 * h;
+                    const uint32_t lo = f32_to_bf16(oacc[mt][4 * qd + 0] * inv) |
+                                        ((uint32_t)f32_to_bf16(oacc[mt][4 * qd + 1] * inv) << 16);
+                    const uint32_t hi = f32_to_bf16(oacc[mt][4 * qd + 2] * inv) |
+                                        ((uint32_t)f32_to_bf16(oacc[mt][4 * qd + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2*>(orow + d) = u32x2{lo, hi};
+                }
+            if (h == 0)
+                w.part_lse[((size_t)t * Hq + head) * kTopK + slot] =
+                    mx * scale_log2 * kLn2 + __logf(sum);
+        }
+    }
+}
+
+// 16 threads per (query, head), 8 dims each: merge the selected slots' partials.
+__global__ __launch_bounds__(256)
+void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
+                          uint16_t* __restrict__ out, float* __restrict__ lse_out, int total_q,
+                          int Hq, int Hkv) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int th = idx / 16;  // t * Hq + h
+    const int part = idx % 16;
+    if (th >= total_q * Hq) return;
+    const int t = th / Hq;
+    const int hh = th % Hq;
+    const int g = hh / (Hq / Hkv);
+    const int32_t* srow = sel + ((size_t)t * Hkv + g) * kTopK;
+    const float* lp = w.part_lse + (size_t)th * kTopK;
+    float mx = -__builtin_inff();
+    for (int i = 0; i < kTopK; ++i)
+        if (srow[i] >= 0) mx = fmaxf(mx, lp[i]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int i = 0; i < kTopK; ++i) {
+        if (srow[i] < 0) continue;
+        const float wi = __expf(lp[i] - mx);
+        den += wi;
+        const u32x4 v = ld16(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] += wi * bf16_to_f32(static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2))));
+    }
+    const float inv = 1.0f / den;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(out + (size_t)th * kHeadDim + 8 * part) = o;
+    if (lse_out && part == 0) lse_out[th] = mx + __logf(den);
+}
+
+}  // namespace
+}  // namespace msa
+
+size_t msa_prefill_ws_bytes(const MsaShape& s, int total_q) {
+    using namespace msa;
+    const int NB = s.B * s.Hkv * s.maxblk;
+    return prefill_ws_size(NB, total_q, s.Hq, s.Hkv);
+}
+
+hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* cu_q, const int32_t* sel, uint16_t* out, float* lse,
+                              void* ws, hipStream_t st) {
+    using namespace msa;
+    if (total_q == 0) return hipSuccess;
+    const int NB = s.B * s.Hkv * s.maxblk;
+    PrefillWs w = prefill_ws(ws, NB, total_q, s.Hq, s.Hkv);
+    const int n_sel = total_q * s.Hkv * kTopK;
+    hipLaunchKernelGGL(zero_kernel, dim3(min(1024, ceil_div(NB, 256))), dim3(256), 0, st,
+                       w.counts, NB, w.cursor, NB);
+    hipLaunchKernelGGL(histogram_kernel, dim3(ceil_div(n_sel, 256)), dim3(256), 0, st, sel, cu_q,
+                       w.counts, s.B, s.Hkv, s.maxblk, n_sel);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, NB);
+    hipLaunchKernelGGL(scatter_kernel, dim3(ceil_div(n_sel, 256)), dim3(256), 0, st, sel, cu_q,
+                       w.offsets, w.cursor, w.entries, s.B, s.Hkv, s.maxblk, n_sel);
+    hipLaunchKernelGGL(block_major_kernel, dim3(NB), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
+                       block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
+                       s.scale * kLog2e);
+    const int nth = total_q * s.Hq * 16;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
+                       out, lse, total_q, s.Hq, s.Hkv);
+    return hipGetLastError();
+}

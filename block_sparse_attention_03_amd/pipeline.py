@@ -1,0 +1,71 @@
+"""One MSA layer-step through the C ABI, with its device buffers.
+
+Decode:  msa_index_score -> msa_topk_blocks -> msa_build_page_table ->
+         msa_sparse_attn_decode.
+Prefill: msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill.
+This module only allocates the outputs and the workspace (torch device memory)
+and calls the library; every step of the computation runs in its kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MsaStep:
+    def __init__(self, x, lse: bool = True):
+        cfg = x.cfg
+        self.x = x
+        self.cfg = cfg
+        self.dims = L.dims_for(cfg)
+        dev = x.q.device
+        T, H, W = cfg.total_q, cfg.num_kv_heads, cfg.max_blocks
+        self.decode = cfg.is_decode
+        self.scores = torch.empty((T, H, W), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((T, H, cfg.topk), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, cfg.num_q_heads), dtype=torch.float32, device=dev) if lse else None
+        if self.decode:
+            R = cfg.num_seqs * H
+            self.page_table = torch.empty((R, cfg.topk), dtype=torch.int32, device=dev)
+            self.row_lens = torch.empty((R,), dtype=torch.int32, device=dev)
+            nbytes = L.msa_decode_workspace_size(self.dims)
+        else:
+            nbytes = L.msa_prefill_workspace_size(self.dims, T)
+        if nbytes == 0:
+            raise L.MsaError(L.MSA_ERROR_NOT_SUPPORTED, "workspace size")
+        self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+
+    def score(self, stream=None):
+        x = self.x
+        L.msa_index_score(self.dims, self.cfg.total_q, x.q_idx, x.kidx_cache, x.block_table,
+                          x.seq_lens, x.cu_q, self.scores, stream)
+
+    def topk(self, stream=None):
+        x = self.x
+        L.msa_topk_blocks(self.dims, self.cfg.total_q, self.scores, x.seq_lens, x.cu_q, self.sel,
+                          stream)
+
+    def page_table_step(self, stream=None):
+        x = self.x
+        L.msa_build_page_table(self.dims, self.sel, x.block_table, x.seq_lens, self.page_table,
+                               self.row_lens, stream)
+
+    def attend(self, stream=None):
+        x = self.x
+        if self.decode:
+            L.msa_sparse_attn_decode(self.dims, x.q, x.k_cache, x.v_cache, self.page_table,
+                                     self.row_lens, self.out, self.lse, self.workspace, stream)
+        else:
+            L.msa_sparse_attn_prefill(self.dims, self.cfg.total_q, x.q, x.k_cache, x.v_cache,
+                                      x.block_table, x.seq_lens, x.cu_q, self.sel, self.out,
+                                      self.lse, self.workspace, stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.topk(stream)
+        if self.decode:
+            self.page_table_step(stream)
+        self.attend(stream)
+        return self.out

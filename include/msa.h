@@ -1,0 +1,188 @@
+/*
+ * msa.h -- C ABI of libmsa.so: MiniMax Sparse Attention (MSA) on one MI355X.
+ *
+ * MSA, as the pages describe it, runs in two stages: a light index branch
+ * scores the KV cache in blocks of Bk = 128 tokens and keeps the top k = 16
+ * blocks per query and GQA KV group; then dense attention runs over the real
+ * (uncompressed) K/V of just those blocks.  Sources, by page and section:
+ *   [aivizor]     edge.aivizor.me news item on the MiniMax M3 serving report --
+ *                 the paragraphs on the two MSA stages, on the KV-Block-Major
+ *                 sparse-attention kernel (outer loop over KV blocks, partial
+ *                 outputs, final Log-Sum-Exp reduction) and on MSA with paged
+ *                 attention in decode (page table from the selected blocks,
+ *                 KV-group dimension flattened into the batch).
+ *   [youmind]     "MiniMax M3: Como la atencion dispersa hace practicos a los
+ *                 agentes de largo alcance" -- MSA figure caption and the bullet
+ *                 "Costo predecible a cualquier longitud" (Bk = 128, k = 16).
+ *   [mechatronic] "MiniMax M3: MoE de 428B con 1M de contexto en Blackwell",
+ *                 section on what makes M3 different (each KV block read once,
+ *                 contiguously; attention on real KV).
+ * The pages do not give the scoring function.  This library fixes it as:
+ * score(block) = max over the block's causally visible tokens of
+ * q_idx . k_idx (idx_dim = 64, fp32 accumulation); blocks after the query's
+ * own block are ineligible; the own block is always kept; ties go to the lower
+ * block index.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory,
+ *     16-byte aligned.  bf16 tensors are passed as raw 16-bit patterns.
+ *   - The caller owns every buffer.  The library allocates nothing on the hot
+ *     path and holds no mutable global state; calls on different streams with
+ *     different buffers may run concurrently.
+ *   - Each call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns without synchronising.
+ *   - Host-side checks (dims, null or misaligned pointers, workspace size) run
+ *     before any launch; on failure the call returns an error status, launches
+ *     nothing and leaves outputs untouched.  The library never aborts, prints
+ *     or throws.  Device-resident CONTENT (seq_lens, cu_q, block_table, sel,
+ *     page_table, row_lens) is a precondition the caller guarantees: page
+ *     indices in [0, num_pages), 1 <= seq_lens[s], 0 <= cu_q[s+1]-cu_q[s] <=
+ *     seq_lens[s], block_table rows cover ceil(seq_lens[s]/Bk) blocks.
+ *   - Same inputs give bit-identical outputs (no float atomics in results).
+ *   - Sequences and positions: sequence s owns query tokens cu_q[s] ..
+ *     cu_q[s+1]-1 (its n_s new tokens), which are the LAST n_s of its
+ *     seq_lens[s] cache tokens: the i-th has absolute position
+ *     p = seq_lens[s] - n_s + i and own block b_loc = p / Bk.  Their K, V and
+ *     k_idx are already in the cache.  Decode is n_s = 1 for every sequence.
+ *   - Token j of sequence s lives in page block_table[s][j / Bk], slot j % Bk.
+ *   - Query head h belongs to KV group h / (H_q / H_kv).
+ *   - Supported sizes: head_dim 128, idx_dim 64, block_size 128, topk 16,
+ *     H_q / H_kv <= 16, num_idx_heads 1 or H_kv, max_blocks_per_seq <= 16384.
+ *     Other values return MSA_ERROR_NOT_SUPPORTED.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum {
+    MSA_SUCCESS = 0,
+    MSA_ERROR_INVALID_VALUE = 1, /* a null/misaligned pointer or inconsistent dims */
+    MSA_ERROR_NOT_SUPPORTED = 2, /* valid, but outside the sizes listed above */
+    MSA_ERROR_WORKSPACE = 3,     /* workspace null or smaller than the size query */
+    MSA_ERROR_LAUNCH = 4         /* the HIP runtime refused a launch */
+} msa_status_t;
+
+typedef struct {
+    int32_t num_seqs;           /* B */
+    int32_t num_q_heads;        /* H_q, a multiple of H_kv */
+    int32_t num_kv_heads;       /* H_kv: KV groups */
+    int32_t num_idx_heads;      /* H_idx: 1 = one index key per token shared by all
+                                   groups; H_kv = one index key per token and group */
+    int32_t head_dim;           /* D = 128 */
+    int32_t idx_dim;            /* d = 64 */
+    int32_t block_size;         /* Bk = 128 (also the page size) */
+    int32_t topk;               /* k = 16 */
+    int32_t max_blocks_per_seq; /* width of block_table and of scores */
+    int32_t num_pages;          /* pages in the K/V/k_idx pools */
+    float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim) */
+} msa_dims_t;
+
+/*
+ * Index-branch block scores ([aivizor] two-stage paragraph; [youmind] MSA
+ * figure caption: the index branch scores the KV blocks).
+ *   q_idx       [total_q, H_kv, 64]        bf16
+ *   kidx_cache  [num_pages, H_idx, 128, 64] bf16
+ *   block_table [B, max_blocks_per_seq]    int32
+ *   seq_lens    [B] int32, cu_q [B+1] int32 (cu_q[0] = 0, cu_q[B] = total_q)
+ *   scores      [total_q, H_kv, max_blocks_per_seq] fp32 (output)
+ * scores[t,g,b] = max_{j in block b, j <= p} sum_i q_idx[t,g,i] * k_idx[j,i]
+ * with fp32 accumulation, where k_idx comes from index head 0 (H_idx = 1) or
+ * g (H_idx = H_kv); -inf for b > b_loc.  total_q = 0 is a no-op.
+ */
+msa_status_t msa_index_score(const msa_dims_t *dims, int32_t total_q, const uint16_t *q_idx,
+                             const uint16_t *kidx_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const int32_t *cu_q, float *scores,
+                             void *stream);
+
+/*
+ * Top-k block selection per (query, KV group) ([youmind] bullet "Costo
+ * predecible a cualquier longitud").  Candidates are blocks 0..b_loc; the own
+ * block b_loc is always kept; the others rank by score, equal scores (with
+ * -0.0 == +0.0) to the lower block index.  min(k, b_loc+1) blocks are kept.
+ *   scores [total_q, H_kv, max_blocks_per_seq] fp32 (entries b > b_loc unread;
+ *          NaN scores are a precondition violation)
+ *   sel    [total_q, H_kv, k] int32 (output): kept blocks in ascending order,
+ *          then -1 padding.
+ */
+msa_status_t msa_topk_blocks(const msa_dims_t *dims, int32_t total_q, const float *scores,
+                             const int32_t *seq_lens, const int32_t *cu_q, int32_t *sel,
+                             void *stream);
+
+/*
+ * Decode page table ([aivizor] paragraph on MSA with paged attention): the
+ * KV-group dimension is flattened into the batch, row r = s*H_kv + g, and the
+ * row's pages are the physical pages of its selected blocks.  Decode only:
+ * one query per sequence, so sel is [B, H_kv, k] (total_q = B).
+ *   page_table [B*H_kv, k] int32 (output): block_table[s][sel[s,g,i]], -1 pad
+ *   row_lens   [B*H_kv]    int32 (output): (n_sel-1)*Bk + (p - Bk*b_loc + 1),
+ *              p = seq_lens[s]-1: with an ascending selection the own, partial
+ *              block is last, so the row reads as a contiguous sequence.
+ */
+msa_status_t msa_build_page_table(const msa_dims_t *dims, const int32_t *sel,
+                                  const int32_t *block_table, const int32_t *seq_lens,
+                                  int32_t *page_table, int32_t *row_lens, void *stream);
+
+/*
+ * Sparse decode attention over the flattened page table ([aivizor] paged-
+ * attention paragraph).  Row r = s*H_kv + g holds the G = H_q/H_kv query heads
+ * q[s, g*G .. g*G+G-1, :] and attends the first row_lens[r] tokens of pages
+ * page_table[r][0..], group g of the K/V pools:
+ *   out = softmax(scale * q K^T) V,  lse = scale-included natural-log LSE.
+ *   q       [B, H_q, 128] bf16;  k_cache, v_cache [num_pages, H_kv, 128, 128] bf16
+ *   out     [B, H_q, 128] bf16 (output, round-to-nearest-even)
+ *   lse     [B, H_q] fp32 (output) or NULL
+ *   workspace: at least msa_decode_workspace_size(dims) bytes of device
+ *   memory, 256-byte aligned; no initial contents required.
+ * 1 <= row_lens[r] <= k*Bk is a precondition.
+ */
+msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, const uint16_t *q,
+                                    const uint16_t *k_cache, const uint16_t *v_cache,
+                                    const int32_t *page_table, const int32_t *row_lens,
+                                    uint16_t *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse prefill attention, KV-block-major ([aivizor] KV-Block-Major
+ * paragraph; [mechatronic]: each KV block read once, contiguously).  The
+ * outer loop runs over (sequence, KV group, block) work items: the block's K
+ * and V are staged once on chip and every (query, head) that selected the
+ * block is attended against it, giving one partial (output, LSE) per
+ * (query, head, selection slot); a Log-Sum-Exp reduction then merges each
+ * query's partials.  The result equals softmax attention over the union of
+ * the selected blocks' tokens, cut at the query position.
+ *   q     [total_q, H_q, 128] bf16; sel [total_q, H_kv, k] int32 (ascending or
+ *         not; -1 entries ignored; entries must be <= b_loc and unique)
+ *   out   [total_q, H_q, 128] bf16 (output); lse [total_q, H_q] fp32 or NULL
+ *   workspace: at least msa_prefill_workspace_size(dims, total_q) bytes,
+ *   256-byte aligned; no initial contents required.
+ */
+msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t total_q, const uint16_t *q,
+                                     const uint16_t *k_cache, const uint16_t *v_cache,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     const int32_t *cu_q, const int32_t *sel, uint16_t *out,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* Workspace sizes in bytes (0 for invalid dims). */
+size_t msa_decode_workspace_size(const msa_dims_t *dims);
+size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);
+
+/* Static, human-readable name of a status code. */
+const char *msa_status_string(msa_status_t status);
+
+/* MSA_ABI_VERSION of the loaded library. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,136 @@
+"""GPU-vs-oracle comparison helpers (imported by the gpu tests).
+
+Protocol for one layer-step on seeded inputs:
+  1. scores: the GPU's dumped fp32 scores against the oracle's fp64 scores,
+     |gpu - ref| <= 1e-4 * max(|ref|, 1), -inf exactly where the oracle has it;
+  2. selection: the oracle's top-k run on the GPU's own dumped scores must
+     equal the GPU's selection bit for bit;
+  3. attention: the oracle's attention run with the GPU's selection against the
+     GPU's out (|gpu - ref| <= 2e-2 + 1e-2 |ref|) and lse (|gpu - ref| <= 5e-3);
+  4. decode: the GPU's page table and row lengths equal the oracle's, bit for bit.
+Large workloads compare sampled rows; the selection check always covers every
+row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from block_sparse_attention_03_amd import inputs as gen
+from block_sparse_attention_03_amd.pipeline import MsaStep
+
+SCORE_RTOL = 1e-4
+OUT_ATOL, OUT_RTOL = 2e-2, 1e-2
+LSE_ATOL = 5e-3
+
+
+def run_step(cfg, poison=False, device="cuda"):
+    print(f"[parity] {cfg.name} seqs={cfg.num_seqs} T={cfg.total_q} Hq={cfg.num_q_heads} "
+          f"Hkv={cfg.num_kv_heads} Hidx={cfg.num_idx_heads} maxblk={cfg.max_blocks}", flush=True)
+    x = gen.make_inputs(cfg, device=device, poison_padding=poison)
+    step = MsaStep(x)
+    step.run()
+    torch.cuda.synchronize()
+    return x, step
+
+
+def _rows_sample(n, max_rows, seed):
+    if n <= max_rows:
+        return np.arange(n, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    r = np.sort(rng.choice(n, size=max_rows, replace=False)).astype(np.int64)
+    r[0], r[-1] = 0, n - 1  # always include both ends
+    return np.unique(r)
+
+
+def compact_pages(x, sel_np, seq_of):
+    """Host copies of just the K/V pages a selection touches.
+
+    Returns (k_pages, v_pages, block_table') where block_table' maps every
+    selected (sequence, block) to its row in the compact pools (others -> 0).
+    """
+    bt = gen.bits(x.block_table)
+    T, H, K = sel_np.shape
+    used = {}
+    for t in range(T):
+        s = int(seq_of[t])
+        for b in np.unique(sel_np[t][sel_np[t] >= 0]):
+            used.setdefault((s, int(b)), None)
+    keys = sorted(used)
+    pages = torch.tensor([int(bt[s, b]) for s, b in keys], dtype=torch.long,
+                         device=x.k_cache.device)
+    kp = gen.bits(x.k_cache.index_select(0, pages)) if len(keys) else np.zeros((1,) + tuple(x.k_cache.shape[1:]), np.uint16)
+    vp = gen.bits(x.v_cache.index_select(0, pages)) if len(keys) else kp
+    bt2 = np.zeros_like(bt)
+    for i, (s, b) in enumerate(keys):
+        bt2[s, b] = i
+    return kp, vp, bt2
+
+
+def check_scores(cfg, x, step, max_rows=4096, seed=0):
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    n = cfg.total_q * cfg.num_kv_heads
+    rows = _rows_sample(n, max_rows, seed)
+    ref = oracle.index_score(gen.bits(x.q_idx), gen.bits(x.kidx_cache), gen.bits(x.block_table),
+                             seq_of, pos_of, cfg.block_size, rows=rows)
+    got = step.scores.reshape(n, -1)[torch.from_numpy(rows).to(step.scores.device)].double().cpu().numpy()
+    ref_inf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ref_inf), "-inf pattern differs"
+    assert np.isfinite(got[~ref_inf]).all(), "non-finite score"
+    err = np.abs(got[~ref_inf] - ref[~ref_inf])
+    bound = SCORE_RTOL * np.maximum(np.abs(ref[~ref_inf]), 1.0)
+    worst = float((err / bound).max()) if err.size else 0.0
+    assert (err <= bound).all(), f"score error {worst:.3g}x the bound"
+    return worst
+
+
+def check_selection(cfg, x, step):
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    H = cfg.num_kv_heads
+    sc = step.scores.double().cpu().numpy().reshape(cfg.total_q * H, -1)
+    want = oracle.topk(sc, oracle.b_loc_rows(pos_of, H, cfg.block_size), cfg.topk)
+    got = step.sel.cpu().numpy().reshape(-1, cfg.topk)
+    bad = np.nonzero((want != got).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:4].tolist()}: " \
+                          f"gpu {got[bad[0]].tolist()} oracle {want[bad[0]].tolist()}"
+    return got.reshape(cfg.total_q, H, cfg.topk)
+
+
+def check_page_table(cfg, x, step):
+    sel = step.sel.cpu().numpy()
+    pt, rl = oracle.page_table(sel, gen.bits(x.block_table), cfg.seq_lens, cfg.block_size)
+    assert np.array_equal(step.page_table.cpu().numpy(), pt), "page table differs"
+    assert np.array_equal(step.row_lens.cpu().numpy(), rl), "row lengths differ"
+
+
+def check_attention(cfg, x, step, max_rows=2048, seed=1):
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    sel = step.sel.cpu().numpy()
+    n = cfg.total_q * cfg.num_q_heads
+    rows = _rows_sample(n, max_rows, seed)
+    kp, vp, bt2 = compact_pages(x, sel, seq_of)
+    ref_o, ref_l = oracle.attention(gen.bits(x.q), kp, vp, bt2, seq_of, pos_of, sel, rows=rows)
+    got_o = step.out.reshape(n, -1).float().cpu().numpy()[rows]
+    got_l = step.lse.reshape(n).cpu().numpy()[rows]
+    assert np.isfinite(got_o).all(), "non-finite output"
+    err = np.abs(got_o - ref_o)
+    lim = OUT_ATOL + OUT_RTOL * np.abs(ref_o)
+    assert (err <= lim).all(), f"out max abs err {err.max():.3g} (worst ratio {(err / lim).max():.3g})"
+    lerr = np.abs(got_l - ref_l)
+    assert (lerr <= LSE_ATOL).all(), f"lse max abs err {lerr.max():.3g}"
+    return float(err.max()), float(lerr.max())
+
+
+def full_check(cfg, poison=False, score_rows=4096, attn_rows=2048):
+    x, step = run_step(cfg, poison)
+    s_err = check_scores(cfg, x, step, score_rows)
+    check_selection(cfg, x, step)
+    if cfg.is_decode:
+        check_page_table(cfg, x, step)
+    o_err, l_err = check_attention(cfg, x, step, attn_rows)
+    print(f"[parity] {cfg.name}: score err/bound {s_err:.3g}, out max abs {o_err:.3g}, "
+          f"lse max abs {l_err:.3g}", flush=True)
+    return x, step

@@ -1,0 +1,127 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_03_amd import _lib as L
+from block_sparse_attention_03_amd import inputs as gen
+from block_sparse_attention_03_amd.pipeline import MsaStep
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def test_native_library_is_loaded():
+    assert L.abi_version() == 1
+    import ctypes
+    assert isinstance(L.lib(), ctypes.CDLL)
+
+
+SMALL = [
+    # decode: several blocks, ragged last pages, permuted pool, GQA 4
+    gen.MsaConfig("decode_ragged_small", [300, 1000, 4500], [1, 1, 1], 12, 3,
+                  permute_pages=True, seed=31),
+    # decode: one token, exactly one block, one block + 1, dense (k*Bk >= L)
+    gen.MsaConfig("decode_edges", [1, 128, 129, 2048, 2049], [1] * 5, 8, 2,
+                  permute_pages=True, extra_pages=3, seed=32),
+    # G = 1 and G = 16
+    gen.MsaConfig("decode_g1", [5000, 700], [1, 1], 4, 4, seed=33),
+    gen.MsaConfig("decode_g16", [3000, 9000], [1, 1], 16, 1, permute_pages=True, seed=34),
+    # prefill: two sequences, partial first/last blocks, several row tiles
+    gen.MsaConfig("prefill_small", [700, 2100], [37, 130], 8, 2, permute_pages=True, seed=35),
+    gen.MsaConfig("prefill_one_block", [100], [100], 6, 1, seed=36),
+    # mixed: a sequence with no new tokens, one decode token, a prefill chunk
+    gen.MsaConfig("mixed_batch", [4000, 900, 3000], [0, 1, 300], 12, 4, permute_pages=True,
+                  seed=37),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_cases_poisoned_padding(cfg):
+    parity.full_check(cfg, poison=True)
+
+
+@pytest.mark.parametrize("cfg", SMALL[:1] + SMALL[4:5], ids=lambda c: c.name)
+def test_per_group_index_keys(cfg):
+    parity.full_check(cfg.with_idx_heads(cfg.num_kv_heads), poison=True)
+
+
+def test_tied_scores_pick_lower_blocks():
+    """Index keys constant per block make scores tie across blocks; the
+    selection must still equal the oracle's on the GPU's own scores."""
+    cfg = gen.MsaConfig("ties", [6000, 3000], [1, 4], 8, 2, seed=38)
+    x = gen.make_inputs(cfg, device="cuda")
+    # every token of a block gets the same key, chosen from 3 values
+    rng = np.random.default_rng(0)
+    vals = torch.from_numpy(rng.integers(0, 3, size=cfg.num_pages).astype(np.float32)).cuda()
+    x.kidx_cache.copy_((vals[:, None, None, None] * 0.5).expand_as(x.kidx_cache).to(torch.bfloat16))
+    x.q_idx.fill_(1.0)
+    step = MsaStep(x)
+    step.run()
+    torch.cuda.synchronize()
+    parity.check_scores(cfg, x, step)
+    sel = parity.check_selection(cfg, x, step)
+    assert (sel >= 0).sum() == cfg.total_q * cfg.num_kv_heads * cfg.topk
+    parity.check_attention(cfg, x, step)
+
+
+def test_closed_forms_constant_v_and_zero_q():
+    cfg = gen.MsaConfig("closed_forms", [5000, 2600], [1, 1], 8, 2, seed=39)
+    x = gen.make_inputs(cfg, device="cuda")
+    x.v_cache.fill_(0.75)
+    step = MsaStep(x)
+    step.run()
+    torch.cuda.synchronize()
+    assert torch.all(step.out.float() == 0.75)
+    # q = 0: every logit is 0, lse = ln(#tokens), out = mean of the attended V
+    x.q.zero_()
+    step.run()
+    torch.cuda.synchronize()
+    n_att = step.row_lens.cpu().numpy().astype(np.float64)
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    want = np.log(np.repeat(n_att, G)).reshape(cfg.num_seqs, cfg.num_q_heads)
+    assert np.allclose(step.lse.cpu().numpy(), want, atol=1e-5)
+
+
+def test_deterministic_and_page_permutation_invariant():
+    base = gen.MsaConfig("perm_a", [7000, 3000, 12000], [1, 1, 1], 12, 2, seed=40)
+    x = gen.make_inputs(base, device="cuda")
+    s1 = MsaStep(x)
+    s1.run()
+    out1, lse1, sc1 = s1.out.clone(), s1.lse.clone(), s1.scores.clone()
+    s1.run()
+    torch.cuda.synchronize()
+    assert torch.equal(out1, s1.out) and torch.equal(lse1, s1.lse)
+    # same logical data, physically permuted pages
+    P = base.num_pages
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(P)).cuda()
+    for name in ("kidx_cache", "k_cache", "v_cache"):
+        t = getattr(x, name)
+        moved = torch.empty_like(t)
+        moved[perm] = t
+        setattr(x, name, moved)
+    x.block_table = perm.to(torch.int32)[x.block_table.long()].contiguous()
+    s2 = MsaStep(x)
+    s2.run()
+    torch.cuda.synchronize()
+    assert torch.equal(sc1, s2.scores)
+    assert torch.equal(out1, s2.out) and torch.equal(lse1, s2.lse)
+
+
+@pytest.mark.parametrize("i", [1, 2, 5])
+def test_decode_workloads(i):
+    cfg = gen.config(i)
+    parity.full_check(cfg, poison=True)
+
+
+def test_decode_1m_context():
+    parity.full_check(gen.config(4))
+
+
+def test_chunked_prefill_64k():
+    parity.full_check(gen.config(3), score_rows=512, attn_rows=1024)
+
+
+def test_paged_decode_60k_per_group_index_keys():
+    parity.full_check(gen.config(2).with_idx_heads(8), poison=True)
