@@ -12,9 +12,10 @@
 // load serves the whole GQA group.  Wavefront w scores tokens 32w..32w+31
 // (S^T = K Q^T, fp32 accumulate); the page's per-head max and sum are
 // combined through LDS; P is rounded to bf16 and shared through LDS; then
-// wavefront w forms dims 32w..32w+31 of O^T = V^T P^T.  V is written to LDS
-// transposed (two tokens per 32-bit word) so the reduction index (tokens) is
-// contiguous for the matrix core.  Each page leaves a normalised partial
+// wavefront w forms dims 32w..32w+31 of O^T = V^T P^T.  V is loaded with
+// fully coalesced 16-byte reads into a row-major LDS tile, and the transposed
+// matrix-core operand (4 consecutive tokens of one dim per lane) comes from
+// the LDS transpose read.  Each page leaves a normalised partial
 // output and its log-sum-exp in the workspace; a second kernel merges a row's
 // pages with the Log-Sum-Exp rule (aivizor, KV-Block-Major paragraph).
 #include "msa_common.hpp"
@@ -23,7 +24,7 @@ namespace msa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kVtStride = kBlock + 8;    // bf16 per transposed-V row (dims x tokens)
+constexpr int kVsStride = kHeadDim + 8;  // bf16 per V row in LDS (tokens x dims)
 constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -47,7 +48,7 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
                         const int32_t* __restrict__ page_table,  // [R, k]
                         const int32_t* __restrict__ row_lens,    // [R]
                         void* __restrict__ ws, int Hq, int Hkv, int R, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kVsStride];
     __shared__ __attribute__((aligned(16))) uint16_t pl[kMaxGroup * kPStride];
     __shared__ float red_max[4][kMaxGroup];
     __shared__ float red_sum[4][kMaxGroup];
@@ -71,17 +72,15 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
     const int n = lane % 16;   // head column (B / result) or row of A
     const int kg = lane / 16;  // lane group
 
-    // V -> LDS, transposed: thread takes token pair tp and 8 dims; tokens at or
-    // past nv are zero so that P = 0 there never meets a non-finite V.
+    // V -> LDS row-major with coalesced 16-byte loads (16 lanes per 256-byte
+    // row); tokens at or past nv are zero so that P = 0 there never meets a
+    // non-finite V.
     {
-        const int tp = tid % 64;
-        u32x4 v0[4], v1[4];
+        u32x4 vv[8];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int d0 = (tid / 64 + 4 * it) * 8;
-            const int t0 = 2 * tp, t1 = 2 * tp + 1;
-            v0[it] = (t0 < nv) ? ld16(vp + t0 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-            v1[it] = (t1 < nv) ? ld16(vp + t1 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        for (int it = 0; it < 8; ++it) {
+            const int tok = tid / 16 + 16 * it;
+            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
         }
         // K operands for this wave's 32 tokens (rows 32w + 16j + n, dims 32i + 8kg)
         bf16x8 ka[2][4];
@@ -89,7 +88,7 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ka[j][i] = as_bf16x8(ld16(kp + (32 * wave + 16 * j + n) * kHeadDim + 32 * i + 8 * kg));
+                ka[j][i] = as_bf16x8(ld16_stream(kp + (32 * wave + 16 * j + n) * kHeadDim + 32 * i + 8 * kg));
         // Q operands: head n of this group, zero beyond G
         bf16x8 qb[4];
         const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
@@ -97,17 +96,9 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
         for (int i = 0; i < 4; ++i)
             qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
 
-        uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int d0 = (tid / 64 + 4 * it) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (v0[it][e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                const uint32_t hi = (v1[it][e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                vt32[((d0 + e) * kVtStride) / 2 + tp] = lo | (hi << 16);
-            }
-        }
+        for (int it = 0; it < 8; ++it)
+            *reinterpret_cast<u32x4*>(vs + (tid / 16 + 16 * it) * kVsStride + 8 * (tid % 16)) = vv[it];
 
         // S^T = K Q^T for tokens 32w + 16j + 4kg + rr, head n
         f32x4 sacc[2];
@@ -165,9 +156,11 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
             const bf16x8 pbv = as_bf16x8(u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const int dim = 32 * wave + 16 * mt + n;
-                const u32x2 v0a = *reinterpret_cast<const u32x2*>(vt + dim * kVtStride + ta);
-                const u32x2 v1a = *reinterpret_cast<const u32x2*>(vt + dim * kVtStride + ta + 16);
+                // lane j of group kg points at token 32ks + 4kg + j/4 (and +16),
+                // dims d0 + 4(j%4); the transpose read hands lane i dim d0 + i
+                const uint16_t* src = vs + (ta + n / 4) * kVsStride + 32 * wave + 16 * mt + 4 * (n % 4);
+                const u32x2 v0a = lds_read_tr16(src);
+                const u32x2 v1a = lds_read_tr16(src + 16 * kVsStride);
                 oacc[mt] = mfma16(as_bf16x8(u32x4{v0a[0], v0a[1], v1a[0], v1a[1]}), pbv, oacc[mt]);
             }
         }
@@ -201,13 +194,22 @@ void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __res
     const int npages = min(kTopK, ceil_div(row_lens[r], kBlock));
     DecodeWs w = decode_ws(const_cast<void*>(ws), R, G);
     const float* lp = w.lse + (size_t)r * kTopK * G + n;
+    // all partials' loads are issued before any is used
+    float li[kTopK], oi[kTopK];
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) {
+        li[i] = (i < npages) ? lp[i * G] : -__builtin_inff();
+        oi[i] = (i < npages) ? w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d] : 0.f;
+    }
     float mx = -__builtin_inff();
-    for (int i = 0; i < npages; ++i) mx = fmaxf(mx, lp[i * G]);
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) mx = fmaxf(mx, li[i]);
     float den = 0.f, acc = 0.f;
-    for (int i = 0; i < npages; ++i) {
-        const float wi = __expf(lp[i * G] - mx);
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) {
+        const float wi = (i < npages) ? __expf(li[i] - mx) : 0.f;
         den += wi;
-        acc += wi * w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d];
+        acc += wi * oi[i];
     }
     const int s = r / Hkv;
     const int h = (r % Hkv) * G + n;

@@ -16,6 +16,16 @@
 // In decode (one query per sequence) the kernel is a single pass over the
 // index-key cache: it is HBM-bound, and the matrix core keeps the ALU work
 // far below the load time.
+//
+// Many queries per sequence (chunked prefill) make scoring a dense
+// contraction, [tokens x 64] . [64 x (query, group) rows], reduced by a max
+// over each 128-token block.  A second kernel handles that case as a GEMM:
+// a workgroup of 8 wavefronts owns 1024 rows of one sequence (their q_idx
+// held in registers as 32x32x16 B operands) and a chunk of 64 blocks; each
+// block's index keys are staged once in LDS (double-buffered, rows padded so
+// the A-operand reads are bank-conflict free) and used by all 8 wavefronts.
+// The epilogue masks tokens past each row's position and keeps per-row block
+// maxima in registers, so the 32x32 products never leave the chip.
 #include "msa_common.hpp"
 
 namespace msa {
@@ -74,7 +84,7 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     for (int mt = 0; mt < 8; ++mt) {
         const uint16_t* row = kb + (mt * 16 + m_in) * kIdxDim;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[mt][i] = as_bf16x8(ld16(row + 32 * i + 8 * kg));
+        for (int i = 0; i < 2; ++i) a[mt][i] = as_bf16x8(ld16_stream(row + 32 * i + 8 * kg));
     }
 
     const int tok0 = b * kBlock;
@@ -112,6 +122,197 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// GEMM form for many queries per sequence
+// ---------------------------------------------------------------------------
+constexpr int kGWaves = 8;                       // wavefronts per workgroup
+constexpr int kGTiles = 4;                       // 32-row tiles per wavefront
+constexpr int kGRows = kGWaves * kGTiles * 32;   // rows per workgroup (1024)
+constexpr int kGBlocks = 64;                     // blocks per workgroup chunk
+constexpr int kGSub = 8;                         // blocks whose maxima are held at once
+constexpr int kKStrideB = kIdxDim * 2 + 16;      // bytes per LDS index-key row (padded)
+
+// Which (sequence, row group) this workgroup serves.  Sequence s has
+// ceil(nq_s * R / kGRows) row groups; group ids are dealt out in sequence order.
+// Returns false if blockIdx.x is past the last group.
+__device__ bool find_row_group(const int32_t* __restrict__ cu_q, int B, int R, int gid, int* s_out,
+                               int* g_out) {
+    const int lane = __lane_id();
+    int base = 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+        const int i = c0 + lane;
+        const int nq = (i < B) ? (cu_q[i + 1] - cu_q[i]) : 0;
+        const int groups = (nq * R + kGRows - 1) / kGRows;
+        int scan = groups;  // inclusive prefix over lanes
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(scan, off, kWave);
+            if (lane >= off) scan += v;
+        }
+        const uint64_t hit = __ballot(base + scan > gid);
+        if (hit) {
+            const int first = __builtin_ctzll(hit);
+            const int prev = __shfl(scan - groups, first, kWave);
+            *s_out = c0 + first;
+            *g_out = gid - base - prev;
+            return true;
+        }
+        base += __shfl(scan, kWave - 1, kWave);
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(kGWaves * kWave)
+void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
+                             const uint16_t* __restrict__ kidx,    // [P, Hidx, 128, 64]
+                             const int32_t* __restrict__ block_table,
+                             const int32_t* __restrict__ seq_lens,
+                             const int32_t* __restrict__ cu_q,
+                             float* __restrict__ scores,           // [T, Hkv, maxblk]
+                             int B, int Hkv, int Hidx, int maxblk) {
+    __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBlock * kKStrideB];
+    __shared__ int grp[2];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int ih = blockIdx.z;
+    const int R = (Hidx == 1) ? Hkv : 1;
+    if (wave == 0) {
+        int s_, g_;
+        const bool ok = find_row_group(cu_q, B, R, blockIdx.x, &s_, &g_);
+        if (lane == 0) {
+            grp[0] = ok ? s_ : -1;
+            grp[1] = g_;
+        }
+    }
+    __syncthreads();
+    const int s = grp[0];
+    if (s < 0) return;  // workgroup-uniform
+    const int rg = grp[1];
+    const int L = seq_lens[s];
+    const int q0 = cu_q[s];
+    const int nq = cu_q[s + 1] - q0;
+    const int nrows = nq * R;
+    const int row0 = rg * kGRows;                       // first row of the workgroup
+    const int row_end = min(nrows, row0 + kGRows);
+    const int p_first = L - nq + row0 / R;              // smallest position in the group
+    const int p_last = L - nq + (row_end - 1) / R;      // largest
+    const int b_begin = blockIdx.y * kGBlocks;
+    const int b_end = min(maxblk, b_begin + kGBlocks);
+    // blocks at or past b_vis_end are after every row's position: -inf
+    const int b_vis_end = min(b_end, p_last / kBlock + 1);
+
+    const int n = lane % 32;  // row within a tile / token within a token tile
+    const int h = lane / 32;  // lane half: dims 32h .. 32h+31 of the reduction
+
+    // B operands: q_idx of this wave's 4 row tiles
+    bf16x8 qb[kGTiles][4];
+    int prow[kGTiles];  // position of each lane's row (per tile)
+    bool rok[kGTiles];
+#pragma unroll
+    for (int r = 0; r < kGTiles; ++r) {
+        const int rho = row0 + (wave * kGTiles + r) * 32 + n;
+        rok[r] = rho < row_end;
+        const int qi = rok[r] ? rho / R : 0;
+        const int g = (Hidx == 1) ? (rok[r] ? rho % R : 0) : ih;
+        prow[r] = L - nq + qi;
+        const uint16_t* qrow = q_idx + ((size_t)(q0 + qi) * Hkv + g) * kIdxDim + 32 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qb[r][i] = as_bf16x8(rok[r] ? ld16(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u});
+    }
+
+    // index-key tile staging: 16 KB per block, two 16-byte pieces per thread
+    auto load_tile = [&](int b, u32x4* v) {
+        const int page = block_table[(size_t)s * maxblk + b];
+        const unsigned char* src =
+            reinterpret_cast<const unsigned char*>(kidx + ((size_t)page * Hidx + ih) * kBlock * kIdxDim);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int c = tid + kGWaves * kWave * it;  // 16-byte piece: row c/8, col c%8
+            v[it] = ld16(src + c * 16);
+        }
+    };
+    auto store_tile = [&](int buf, const u32x4* v) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int c = tid + kGWaves * kWave * it;
+            *reinterpret_cast<u32x4*>(&ktile[buf][(c / 8) * kKStrideB + (c % 8) * 16]) = v[it];
+        }
+    };
+
+    u32x4 stage[2];
+    if (b_begin < b_vis_end) {
+        load_tile(b_begin, stage);
+        store_tile(0, stage);
+    }
+    __syncthreads();
+
+    for (int sub = b_begin; sub < b_end; sub += kGSub) {
+        float mx[kGTiles][kGSub];
+#pragma unroll
+        for (int bb = 0; bb < kGSub; ++bb) {
+            const int b = sub + bb;
+#pragma unroll
+            for (int r = 0; r < kGTiles; ++r) mx[r][bb] = -__builtin_inff();
+            if (b >= b_vis_end) continue;  // workgroup-uniform
+            const int buf = (b - b_begin) & 1;
+            const bool more = b + 1 < b_vis_end;
+            if (more) load_tile(b + 1, stage);
+            const unsigned char* kt = ktile[buf];
+            const int tok_base = b * kBlock;
+            const bool need_mask = tok_base + kBlock - 1 > p_first;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                bf16x8 a[4];
+                const unsigned char* arow = kt + (32 * tt + n) * kKStrideB + 64 * h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * i));
+#pragma unroll
+                for (int r = 0; r < kGTiles; ++r) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = mfma32(a[i], qb[r][i], acc);
+                    float m = -__builtin_inff();
+                    if (need_mask) {
+                        // value v is token tok_base + 32tt + 8(v/4) + 4h + v%4 of row n
+                        const int lim = prow[r] - tok_base - 32 * tt - 4 * h;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[v] : -__builtin_inff());
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[v]);
+                    }
+                    mx[r][bb] = fmaxf(mx[r][bb], m);
+                }
+            }
+            if (more) store_tile(buf ^ 1, stage);
+            __syncthreads();
+        }
+        // both lane halves saw different tokens of the same row: combine, then
+        // half h writes blocks 4h .. 4h+3 of the sub-chunk
+#pragma unroll
+        for (int r = 0; r < kGTiles; ++r) {
+#pragma unroll
+            for (int bb = 0; bb < kGSub; ++bb) mx[r][bb] = fmaxf(mx[r][bb], __shfl_xor(mx[r][bb], 32, kWave));
+            if (!rok[r]) continue;
+            const int rho = row0 + (wave * kGTiles + r) * 32 + n;
+            const int t = q0 + rho / R;
+            const int g = (Hidx == 1) ? rho % R : ih;
+            float* dst = scores + ((size_t)t * Hkv + g) * maxblk;
+#pragma unroll
+            for (int bb = 0; bb < kGSub / 2; ++bb) {
+                const int b = sub + 4 * h + bb;
+                const float v = h ? mx[r][4 + bb] : mx[r][bb];
+                if (b < b_end) dst[b] = v;
+            }
+        }
+    }
+}
+
 }  // namespace
 }  // namespace msa
 
@@ -121,6 +322,16 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
                                   hipStream_t st) {
     using namespace msa;
     if (total_q == 0) return hipSuccess;
+    const int R = (s.Hidx == 1) ? s.Hkv : 1;
+    if (total_q > 4 * s.B) {
+        // many queries per sequence on average: GEMM form.  Upper bound on the
+        // number of row groups: sum_s ceil(nq_s R / rows) <= total_q R / rows + B.
+        const int groups = ceil_div(total_q * R, kGRows) + s.B;
+        dim3 grid(groups, ceil_div(s.maxblk, kGBlocks), s.Hidx);
+        hipLaunchKernelGGL(index_score_gemm_kernel, grid, dim3(kGWaves * kWave), 0, st, q_idx, kidx,
+                           block_table, seq_lens, cu_q, scores, s.B, s.Hkv, s.Hidx, s.maxblk);
+        return hipGetLastError();
+    }
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
     hipLaunchKernelGGL(index_score_kernel, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
                        block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk);

@@ -40,6 +40,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// 16-byte load of data that is read once (K/V pages, index keys): the
+// nontemporal hint keeps it from displacing reusable lines in the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // 8 fp32 -> 8 bf16 (RNE) packed for a matrix-core operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
                                               float a5, float a6, float a7) {
@@ -72,6 +78,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the LDS address of 4 consecutive bf16 values; lane i
+// receives element i%4 of the values supplied by lanes i/4, i/4+4, i/4+8 and
+// i/4+12 (in that order).  With lane j pointing at row R0 + j/4, columns
+// C0 + 4*(j%4) .. +3 of a row-major tile, lane i therefore receives column
+// C0 + i of rows R0 .. R0+3: a column slice, i.e. the transposed operand.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds_ptr));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, kWave));

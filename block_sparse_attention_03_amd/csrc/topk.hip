@@ -32,14 +32,31 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Sequence of query token t by binary search over cu_q (wave-uniform).
-__device__ __forceinline__ int seq_of_token(const int32_t* cu_q, int B, int t) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+struct SeqInfo {
+    int q0, nq, L;  // first query token, query count and cache length of the sequence
+};
+
+// Sequence of the wave-uniform query token t.  Lanes read cu_q / seq_lens of
+// 64 sequences at once and a ballot counts the sequences that end at or before
+// t, so a batch of up to 64 sequences costs one round of loads.  t < cu_q[B].
+__device__ __forceinline__ SeqInfo lookup_seq(const int32_t* __restrict__ cu_q,
+                                              const int32_t* __restrict__ seq_lens, int B, int t) {
+    const int lane = __lane_id();
+    for (int base = 0;; base += kWave) {
+        const int i = base + lane;
+        const bool ok = i < B;
+        const int c0 = ok ? cu_q[i] : 0;
+        const int c1 = ok ? cu_q[i + 1] : 0x7FFFFFFF;
+        const int L = ok ? seq_lens[i] : 0;
+        const int cnt = __popcll(__ballot(c1 <= t));
+        if (cnt < kWave || base + kWave >= B) {
+            SeqInfo r;
+            r.q0 = __shfl(c0, cnt, kWave);
+            r.nq = __shfl(c1, cnt, kWave) - r.q0;
+            r.L = __shfl(L, cnt, kWave);
+            return r;
+        }
     }
-    return lo;
 }
 
 // W wavefronts per row; when W == 1, each of the 4 wavefronts of a workgroup
@@ -65,14 +82,21 @@ void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ s
     if (row >= total_rows) return;  // W == 1 only: whole wavefront leaves together
 
     const int t = row / Hkv;
-    const int s = seq_of_token(cu_q, B, t);
-    const int nq = cu_q[s + 1] - cu_q[s];
-    const int p = seq_lens[s] - nq + (t - cu_q[s]);
+    const float* sc = scores + (size_t)row * maxblk;
+    // score loads do not wait for the sequence lookup: every slot below maxblk
+    // is in the row; slots past the own block are discarded below
+    float raw[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int c = i * kThreads + w * kWave + lane;
+        raw[i] = (c < maxblk) ? sc[c] : 0.f;
+    }
+    const SeqInfo si = lookup_seq(cu_q, seq_lens, B, t);
+    const int p = si.L - si.nq + (t - si.q0);
     const int b_loc = p / kBlock;
     const int ncand = b_loc + 1;
     const int kk = ncand < kTopK ? ncand : kTopK;
     int32_t* out = sel + (size_t)row * kTopK;
-    const float* sc = scores + (size_t)row * maxblk;
 
     if (ncand <= kTopK) {  // every eligible block is kept
         if (w == 0 && lane < kTopK) out[lane] = (lane < ncand) ? lane : -1;
@@ -84,7 +108,7 @@ void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ s
     for (int i = 0; i < NPT; ++i) {
         const int c = i * kThreads + w * kWave + lane;
         uint32_t k = 0u;
-        if (c < b_loc) k = order_key(sc[c]);
+        if (c < b_loc) k = order_key(raw[i]);
         else if (c == b_loc) k = 0xFFFFFFFFu;
         key[i] = k;
     }

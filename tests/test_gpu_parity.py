@@ -125,3 +125,40 @@ def test_chunked_prefill_64k():
 
 def test_paged_decode_60k_per_group_index_keys():
     parity.full_check(gen.config(2).with_idx_heads(8), poison=True)
+
+
+@pytest.mark.parametrize("prefill", [False, True], ids=["decode", "prefill"])
+def test_graph_replay_matches_eager(prefill):
+    """The layer-step captured as one HIP graph: every replay, with eager work
+    and synchronisation between replays, equals the eager result bit for bit."""
+    cfg = (gen.MsaConfig("graph_prefill", [3000, 900], [200, 64], 12, 4, permute_pages=True,
+                         seed=41) if prefill else
+           gen.MsaConfig("graph_decode", [9000, 700, 4096], [1, 1, 1], 12, 4,
+                         permute_pages=True, seed=42))
+    x = gen.make_inputs(cfg, device="cuda")
+    step = MsaStep(x)
+    step.run()
+    torch.cuda.synchronize()
+    ref_out, ref_lse, ref_sel = step.out.clone(), step.lse.clone(), step.sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    torch.cuda.synchronize()
+    for i in range(4):
+        step.out.zero_()
+        step.sel.fill_(-7)
+        step.run()  # eager work between replays
+        torch.cuda.synchronize()
+        step.out.zero_()
+        step.sel.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, ref_out), f"replay {i}: out differs"
+        assert torch.equal(step.lse, ref_lse), f"replay {i}: lse differs"
+        assert torch.equal(step.sel, ref_sel), f"replay {i}: sel differs"
