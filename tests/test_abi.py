@@ -1,0 +1,120 @@
+"""Host-only checks of libmsa.so (no kernel launch, no GPU needed).
+
+The library must load, export every entry point include/msa.h declares, and
+reject bad arguments on the host with the documented status before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_03_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "msa.h")
+P = ctypes.c_void_p
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(L.EXPORTED) == declared_entry_points()
+
+
+def test_every_declared_symbol_is_exported():
+    lib = L.lib()
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert L.abi_version() == 1
+    assert L.status_string(L.MSA_SUCCESS) == "MSA_SUCCESS"
+    assert L.status_string(L.MSA_ERROR_WORKSPACE) == "MSA_ERROR_WORKSPACE"
+    assert L.status_string(99) == "MSA_ERROR_UNKNOWN"
+
+
+def dims(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, max_blocks_per_seq=10, num_pages=20)
+    base.update(kw)
+    return L.make_dims(**base)
+
+
+def test_workspace_sizes():
+    d = dims()
+    assert L.msa_decode_workspace_size(d) >= 2 * 2 * 16 * 4 * 129 * 4
+    assert L.msa_decode_workspace_size(d) % 256 == 0
+    assert L.msa_prefill_workspace_size(d, 100) > 100 * 8 * 16 * 128 * 2
+    assert L.msa_decode_workspace_size(dims(head_dim=64)) == 0
+    assert L.msa_prefill_workspace_size(d, -1) == 0
+
+
+# fake, aligned, non-null device addresses: every call below fails a host
+# check before it could launch anything
+A = P(0x100000)
+MIS = P(0x100002)
+
+
+def call_score(d, total_q=4, **ptr):
+    args = dict(q_idx=A, kidx=A, bt=A, sl=A, cu=A, sc=A)
+    args.update(ptr)
+    return L.lib().msa_index_score(ctypes.byref(d) if d is not None else None, total_q,
+                                   args["q_idx"], args["kidx"], args["bt"], args["sl"],
+                                   args["cu"], args["sc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), L.MSA_ERROR_NOT_SUPPORTED),
+    (dict(idx_dim=128), L.MSA_ERROR_NOT_SUPPORTED),
+    (dict(block_size=64), L.MSA_ERROR_NOT_SUPPORTED),
+    (dict(topk=8), L.MSA_ERROR_NOT_SUPPORTED),
+    (dict(num_q_heads=34, num_kv_heads=2), L.MSA_ERROR_NOT_SUPPORTED),   # G = 17
+    (dict(max_blocks_per_seq=16385), L.MSA_ERROR_NOT_SUPPORTED),
+    (dict(num_q_heads=9), L.MSA_ERROR_INVALID_VALUE),                     # H_q % H_kv
+    (dict(num_idx_heads=3), L.MSA_ERROR_INVALID_VALUE),
+    (dict(num_kv_heads=0), L.MSA_ERROR_INVALID_VALUE),
+    (dict(num_pages=0), L.MSA_ERROR_INVALID_VALUE),
+    (dict(softmax_scale=float("nan")), L.MSA_ERROR_INVALID_VALUE),
+])
+def test_index_score_rejects_bad_dims(kw, status):
+    # dims are checked before pointers; a null q_idx guarantees that no call
+    # here can ever reach a launch
+    assert call_score(dims(**kw), q_idx=None) == status
+
+
+def test_null_and_misaligned_pointers():
+    assert call_score(None) == L.MSA_ERROR_INVALID_VALUE
+    assert call_score(dims(), q_idx=None) == L.MSA_ERROR_INVALID_VALUE
+    assert call_score(dims(), q_idx=MIS) == L.MSA_ERROR_INVALID_VALUE
+    assert call_score(dims(), total_q=-1) == L.MSA_ERROR_INVALID_VALUE
+    lib = L.lib()
+    d = dims()
+    assert lib.msa_topk_blocks(ctypes.byref(d), 4, None, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_build_page_table(ctypes.byref(d), A, A, A, None, A, None) == L.MSA_ERROR_INVALID_VALUE
+
+
+def test_decode_and_prefill_workspace_errors():
+    lib = L.lib()
+    d = dims()
+    need = L.msa_decode_workspace_size(d)
+    # null, short, and misaligned workspaces
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), A, A, A, A, A, A, A, None, need, None) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), A, A, A, A, A, A, A, A, need - 1, None) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), A, A, A, A, A, A, A, P(0x100010), need, None) == L.MSA_ERROR_WORKSPACE
+    # misaligned bf16 output
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), A, A, A, A, A, MIS, A, A, need, None) == L.MSA_ERROR_INVALID_VALUE
+    need_p = L.msa_prefill_workspace_size(d, 7)
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(d), 7, A, A, A, A, A, A, A, A, A, A, need_p - 256, None) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(d), 7, A, A, A, A, A, A, None, A, A, A, need_p, None) == L.MSA_ERROR_INVALID_VALUE
+
+
+def test_binding_checks_tensors_before_calling():
+    import torch
+    d = dims()
+    cpu = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.msa_index_score(d, 4, cpu, cpu, cpu, cpu, cpu, cpu)
