@@ -24,7 +24,8 @@ namespace msa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kVsStride = kHeadDim + 8;  // bf16 per V row in LDS (tokens x dims)
+constexpr int kVsStride = kHeadDim + 32; // bf16 per V row in LDS (tokens x dims); 320 B keeps the
+                                         // transpose reads of 4 rows x 64 B on distinct banks
 constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

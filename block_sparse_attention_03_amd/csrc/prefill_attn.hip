@@ -12,11 +12,13 @@
 //   1. inverse map: histogram of (sequence, group, block) buckets over the
 //      selection, exclusive scan, scatter of (query, slot) entries;
 //   2. block-major attention: one workgroup per bucket stages the block's K
-//      (row-major) and V (transposed) in LDS once, then its wavefronts sweep
+//      and V (row-major, coalesced loads) in LDS once, then its wavefronts sweep
 //      the bucket's (query, head) rows 32 at a time with 32x32x16 bf16 matrix
 //      cores: S^T = K Q^T, row softmax in registers, P rounded to bf16 and
 //      fed straight from the S^T accumulators as the B operand of
-//      O^T = V^T P^T.  Each (query, head, slot) gets a normalised bf16 partial
+//      O^T = V^T P^T, whose V^T operand comes from LDS transpose reads.  The
+//      next row tile's query gathers are issued before the current tile's
+//      softmax, hiding their latency.  Each (query, head, slot) gets a normalised bf16 partial
 //      output and an fp32 log-sum-exp;
 //   3. merge: per (query, head), the partials of its selected slots combine in
 //      slot order (deterministic; no float atomics).
@@ -25,9 +27,11 @@
 namespace msa {
 namespace {
 
-constexpr int kPfThreads = 256;
-constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS
-constexpr int kVtStride = kBlock + 8;    // bf16 per transposed-V row in LDS
+constexpr int kPfThreads = 512;
+constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-byte reads of 8
+                                         // consecutive rows hit distinct banks)
+constexpr int kVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B: the transpose reads
+                                         // of 4 consecutive rows x 64 B hit distinct banks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -134,7 +138,7 @@ __global__ void scatter_kernel(const int32_t* __restrict__ sel, const int32_t* _
     entries[pos] = (t << 4) | slot;
 }
 
-__global__ __launch_bounds__(kPfThreads)
+__global__ __launch_bounds__(kPfThreads, 1)
 void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
                         const uint16_t* __restrict__ v_cache,
@@ -143,7 +147,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                         const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
                         int maxblk, float scale_log2) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[kBlock * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kVStride];
+    // per-wave staging of 32 query rows in, then 32 partial-output rows out
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[(kPfThreads / kWave) * 32 * kKStride];
 
     const int bk = blockIdx.x;
     const int cnt = w.counts[bk];
@@ -163,30 +169,24 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const uint16_t* vp = v_cache + page_off;
     const int tid = threadIdx.x;
 
-    // Stage the block once: K row-major, V transposed (dims x tokens); tokens
-    // past the sequence end are zero.
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int c = tid + kPfThreads * it;
-        const int tok = c / 16, d0 = (c % 16) * 8;
-        const u32x4 v = (tok < nv) ? ld16(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(ks + tok * kKStride + d0) = v;
-    }
+    // Stage the block once, K and V both row-major with coalesced 16-byte
+    // loads; tokens past the sequence end are zero.
     {
-        const int tp = tid % 64;
-        uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
+        constexpr int kIt = kBlock * kHeadDim / 8 / kPfThreads;
+        u32x4 kv[kIt], vv[kIt];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int d0 = (tid / 64 + 4 * it) * 8;
-            const int t0 = 2 * tp, t1 = 2 * tp + 1;
-            const u32x4 v0 = (t0 < nv) ? ld16(vp + t0 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 v1 = (t1 < nv) ? ld16(vp + t1 * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        for (int it = 0; it < kIt; ++it) {
+            const int c = tid + kPfThreads * it;
+            const int tok = c / 16, d0 = (c % 16) * 8;
+            kv[it] = (tok < nv) ? ld16_stream(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (v0[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                const uint32_t hi = (v1[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                vt32[((d0 + e) * kVtStride) / 2 + tp] = lo | (hi << 16);
-            }
+        for (int it = 0; it < kIt; ++it) {
+            const int c = tid + kPfThreads * it;
+            const int tok = c / 16, d0 = (c % 16) * 8;
+            *reinterpret_cast<u32x4*>(ks + tok * kKStride + d0) = kv[it];
+            *reinterpret_cast<u32x4*>(vs + tok * kVStride + d0) = vv[it];
         }
     }
     __syncthreads();
@@ -197,40 +197,87 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int h = lane / 32;   // lane half
     const int nrows = cnt * G;
     const int tok0 = b * kBlock;
+    constexpr int kWaves = kPfThreads / kWave;
+    uint16_t* tbuf = tiles + wave * 32 * kKStride;  // this wave's 32-row staging tile
 
-    for (int tile = wave; tile * 32 < nrows; tile += kPfThreads / kWave) {
-        const int rho = tile * 32 + n;
-        const bool row_ok = rho < nrows;
-        const int e_idx = row_ok ? rho / G : 0;
-        const int rr_head = row_ok ? rho % G : 0;
-        const int entry = w.entries[base + e_idx];
-        const int t = entry >> 4;
-        const int slot = entry & 15;
-        const int head = g * G + rr_head;
-        const int p = pos0 + t;
+    // Row n of a tile: its query, head and selection slot.  Rows past the
+    // bucket repeat its last row (real data; results discarded).
+    auto row_info = [&](int tile, int* t_out, int* head_out, int* slot_out) {
+        const int rho0 = tile * 32 + n;
+        const int rho = rho0 < nrows ? rho0 : nrows - 1;
+        const int entry = w.entries[base + rho / G];
+        *t_out = entry >> 4;
+        *slot_out = entry & 15;
+        *head_out = g * G + rho % G;
+        return rho0 < nrows;
+    };
+    // Coalesced gather of a tile's 32 query rows: instruction it moves rows
+    // 4it .. 4it+3, 16 lanes x 16 bytes each.
+    auto gather_q = [&](int t_n, int head_n, u32x4* raw) {
+        const int qrow = t_n * Hq + head_n;  // row n's q row (< 2^27)
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = lane / 16 + 4 * it;
+            const size_t off = (size_t)__shfl(qrow, r, kWave) * kHeadDim;
+            raw[it] = ld16(q + off + 8 * (lane % 16));
+        }
+    };
 
-        // Q^T operand: k-step i of lane half h takes dims 64h + 8i .. +7
+    int tile = wave;
+    int t = 0, head = 0, slot = 0;
+    bool row_ok = false;
+    u32x4 qraw[8];
+    if (tile * 32 < nrows) {
+        row_ok = row_info(tile, &t, &head, &slot);
+        gather_q(t, head, qraw);
+    }
+
+    for (; tile * 32 < nrows; tile += kWaves) {
+        // Q rows -> staging tile -> B operands (k-step i of lane half h: dims 64h + 8i .. +7)
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+            *reinterpret_cast<u32x4*>(tbuf + (lane / 16 + 4 * it) * kKStride + 8 * (lane % 16)) = qraw[it];
+        __builtin_amdgcn_wave_barrier();
         bf16x8 qb[8];
-        const uint16_t* qrow = q + ((size_t)t * Hq + head) * kHeadDim + 64 * h;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            qb[i] = as_bf16x8(row_ok ? ld16(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u});
+            qb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(tbuf + n * kKStride + 64 * h + 8 * i));
+        const int cur_t = t, cur_slot = slot, cur_head = head;
+        const bool cur_ok = row_ok;
+        // next tile's rows are gathered while this one computes
+        const int next = tile + kWaves;
+        if (next * 32 < nrows) {
+            row_ok = row_info(next, &t, &head, &slot);
+            gather_q(t, head, qraw);
+        }
 
         // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
-        // token 32mt + 8(v/4) + 4h + v%4 of row n.
+        // token 32mt + 8(v/4) + 4h + v%4 of row n.  Operands of token tile
+        // mt+1 are read while tile mt multiplies.
         f32x16 sacc[4];
+        u32x4 ka[2][8];
+        {
+            const uint16_t* krow = ks + n * kKStride + 64 * h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ka[0][i] = *reinterpret_cast<const u32x4*>(krow + 8 * i);
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            sacc[mt] = f32x16{};
-            const uint16_t* krow = ks + (32 * mt + n) * kKStride + 64 * h;
+            if (mt < 3) {
+                const uint16_t* krow = ks + (32 * (mt + 1) + n) * kKStride + 64 * h;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                sacc[mt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * i)), qb[i],
-                                  sacc[mt]);
+                for (int i = 0; i < 8; ++i) ka[(mt + 1) & 1][i] = *reinterpret_cast<const u32x4*>(krow + 8 * i);
+            }
+            sacc[mt] = mfma32(as_bf16x8(ka[mt & 1][0]), qb[0], f32x16{});
+#pragma unroll
+            for (int i = 1; i < 8; ++i) sacc[mt] = mfma32(as_bf16x8(ka[mt & 1][i]), qb[i], sacc[mt]);
+            // keep the scheduler from hoisting further tiles' operand reads
+            __builtin_amdgcn_sched_barrier(0);
         }
+
         // causal cut inside the query's own block
-        const int lim = p - tok0;  // token index (within block) must be <= lim
-        if (lim < kBlock - 1) {
+        const int lim = pos0 + cur_t - tok0;  // token index (within block) must be <= lim
+        if (__ballot(lim < kBlock - 1)) {  // only tiles holding a row of this block's own queries
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -245,53 +292,83 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[mt][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float mscaled = mx * scale_log2;
 
-        // P (bf16) as B operands of O^T = V^T P^T; k-step i covers tokens
-        // 16i..16i+15 = accumulator values 8(i%2)..8(i%2)+7 of tile i/2.
+        // P first (the S^T registers die as P is built), then O^T = V^T P^T.
+        // k-step i covers tokens 16i..16i+15: the B operand is accumulator
+        // values 8(i%2)..8(i%2)+7 of S^T tile i/2 (tokens 16i + 4h + 0..3 and
+        // 16i + 8 + 4h + 0..3) rounded to bf16; the row sum uses the rounded
+        // weights the product uses.
         bf16x8 pb[8];
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            u32x4 pw;
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-                const float pv = __builtin_amdgcn_exp2f((sacc[i / 2][8 * (i % 2) + e2] - mx) * scale_log2);
-                const __bf16 pbf = static_cast<__bf16>(pv);
-                pb[i][e2] = pbf;
-                sum += static_cast<float>(pbf);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = __builtin_amdgcn_exp2f(sacc[i / 2][8 * (i % 2) + 2 * e2] * scale_log2 - mscaled);
+                const float p1 = __builtin_amdgcn_exp2f(sacc[i / 2][8 * (i % 2) + 2 * e2 + 1] * scale_log2 - mscaled);
+                pw[e2] = pack2_bf16(p0, p1);
+                sum += bf16_lo(pw[e2]) + bf16_hi(pw[e2]);
             }
+            pb[i] = as_bf16x8(pw);
+        }
+        // A operand: the same tokens of dims 32mt + n, from transpose reads of
+        // row-major V (lanes 16*(lane/16) .. +15 read dims 32mt +
+        // 16*((lane/16)%2) .. +15); dim tile mt+1 is read while mt multiplies.
+        f32x16 oacc[4];
+        const int j = lane % 16;
+        const uint16_t* vsrc = vs + (4 * h + j / 4) * kVStride + 16 * ((lane / 16) % 2) + 4 * (j % 4);
+        u32x2 va[2][16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            va[0][2 * i] = lds_read_tr16(vsrc + 16 * i * kVStride);
+            va[0][2 * i + 1] = lds_read_tr16(vsrc + (16 * i + 8) * kVStride);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if (mt < 3) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    va[(mt + 1) & 1][2 * i] = lds_read_tr16(vsrc + 16 * i * kVStride + 32 * (mt + 1));
+                    va[(mt + 1) & 1][2 * i + 1] = lds_read_tr16(vsrc + (16 * i + 8) * kVStride + 32 * (mt + 1));
+                }
+            }
+            const u32x2* a = va[mt & 1];
+            oacc[mt] = mfma32(as_bf16x8(u32x4{a[0][0], a[0][1], a[1][0], a[1][1]}), pb[0], f32x16{});
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                oacc[mt] = mfma32(as_bf16x8(u32x4{a[2 * i][0], a[2 * i][1], a[2 * i + 1][0], a[2 * i + 1][1]}),
+                                  pb[i], oacc[mt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         sum += __shfl_xor(sum, 32, kWave);
 
-        f32x16 oacc[4];
+        // normalised partial output: O^T fragments -> staging tile (row n) ->
+        // coalesced 16-byte stores of 4 rows x 256 bytes per instruction
+        const float inv = 1.0f / sum;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            oacc[mt] = f32x16{};
-            const uint16_t* vrow = vt + (32 * mt + n) * kVtStride + 4 * h;
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 16 * i);
-                const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 * i + 8);
-                oacc[mt] = mfma32(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb[i], oacc[mt]);
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = 32 * mt + 8 * qd + 4 * h;
+                *reinterpret_cast<u32x2*>(tbuf + n * kKStride + d) =
+                    u32x2{pack2_bf16(oacc[mt][4 * qd + 0] * inv, oacc[mt][4 * qd + 1] * inv),
+                          pack2_bf16(oacc[mt][4 * qd + 2] * inv, oacc[mt][4 * qd + 3] * inv)};
             }
-        }
-        if (row_ok) {
-            const float inv = 1.0f / sum;
-            uint16_t* orow = w.part_o + (((size_t)t * Hq + head) * kTopK + slot) * kHeadDim;
+        __builtin_amdgcn_wave_barrier();
+        // partial row index (t * Hq + head) * k + slot < 2^31, or -1 for padding rows
+        const int orow = cur_ok ? (cur_t * Hq + cur_head) * kTopK + cur_slot : -1;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int d = 32 * mt + 8 * qd + 4 * h;
-                    const uint32_t lo = f32_to_bf16(oacc[mt][4 * qd + 0] * inv) |
-                                        ((uint32_t)f32_to_bf16(oacc[mt][4 * qd + 1] * inv) << 16);
-                    const uint32_t hi = f32_to_bf16(oacc[mt][4 * qd + 2] * inv) |
-                                        ((uint32_t)f32_to_bf16(oacc[mt][4 * qd + 3] * inv) << 16);
-                    *reinterpret_cast<u32x2*>(orow + d) = u32x2{lo, hi};
-                }
-            if (h == 0)
-                w.part_lse[((size_t)t * Hq + head) * kTopK + slot] =
-                    mx * scale_log2 * kLn2 + __logf(sum);
+        for (int it = 0; it < 8; ++it) {
+            const int r = lane / 16 + 4 * it;
+            const int o = __shfl(orow, r, kWave);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(tbuf + r * kKStride + 8 * (lane % 16));
+            if (o >= 0) *reinterpret_cast<u32x4*>(w.part_o + (size_t)o * kHeadDim + 8 * (lane % 16)) = v;
         }
+        if (cur_ok && h == 0)
+            w.part_lse[((size_t)cur_t * Hq + cur_head) * kTopK + cur_slot] = mx * scale_log2 * kLn2 + __logf(sum);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -309,25 +386,37 @@ void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
     const int g = hh / (Hq / Hkv);
     const int32_t* srow = sel + ((size_t)t * Hkv + g) * kTopK;
     const float* lp = w.part_lse + (size_t)th * kTopK;
+    // every slot's loads are issued before any is used
+    int bsel[kTopK];
+    float li[kTopK];
+    u32x4 oi[kTopK];
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) bsel[i] = srow[i];
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) {
+        li[i] = bsel[i] >= 0 ? lp[i] : -__builtin_inff();
+        oi[i] = bsel[i] >= 0 ? ld16_stream(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part)
+                             : u32x4{0u, 0u, 0u, 0u};
+    }
     float mx = -__builtin_inff();
-    for (int i = 0; i < kTopK; ++i)
-        if (srow[i] >= 0) mx = fmaxf(mx, lp[i]);
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) mx = fmaxf(mx, li[i]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int i = 0; i < kTopK; ++i) {
-        if (srow[i] < 0) continue;
-        const float wi = __expf(lp[i] - mx);
-        den += wi;
-        const u32x4 v = ld16(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[e] += wi * bf16_to_f32(static_cast<uint16_t>(v[e / 2] >> (16 * (e % 2))));
+    for (int i = 0; i < kTopK; ++i) {
+        const float wi = bsel[i] >= 0 ? __expf(li[i] - mx) : 0.f;
+        den += wi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += wi * bf16_lo(oi[i][e]);
+            acc[2 * e + 1] += wi * bf16_hi(oi[i][e]);
+        }
     }
     const float inv = 1.0f / den;
     u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        o[e] = f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+    for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
     *reinterpret_cast<u32x4*>(out + (size_t)th * kHeadDim + 8 * part) = o;
     if (lse_out && part == 0) lse_out[th] = mx + __logf(den);
 }
