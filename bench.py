@@ -4,16 +4,19 @@
 Headline workload: paged decode, 8 sequences at a 60,000-token cached prefix,
 H_q = 48, H_kv = 8, head_dim 128, idx_dim 64, Bk = 128, k = 16, physical pages
 randomly permuted, keys given a per-block scale (seeded synthetic bf16 data).
-A step is the whole hot path: msa_index_score -> msa_topk_blocks ->
-msa_build_page_table -> msa_sparse_attn_decode, inputs resident in HBM.
+A step is the whole hot path -- scoring, top-k, page table, sparse attention,
+merge -- with inputs resident in HBM.  ``value`` times the fused entry point
+msa_decode_step; the four separate calls msa_index_score -> msa_topk_blocks ->
+msa_build_page_table -> msa_sparse_attn_decode (bit-identical results) are
+timed alongside.
 
-Timing.  Every timed step starts from a cold cache: a 1 GiB read pass runs
-before it (untimed), so the step's inputs come from HBM and not from the
-256 MB Infinity Cache.  Each step is bracketed by HIP events on the stream
-the kernels run on; ``value`` is the mean over the K timed steps of the step
-replayed as one HIP graph.  The same steps launched eagerly, and warm-cache
-back-to-back rates, are reported alongside.  The roofline kernel's duration
-comes from events around its own call in the eager cold pass.
+Timing.  The workload is instantiated for several layers, each with its own
+K/V and index-key caches (together several times the 256 MB Infinity Cache),
+and K layer-steps run back to back cycling over the layers, as a decode pass
+over a model does: every step reads its inputs from HBM, and kernels follow
+each other with no host or timing gaps.  One pair of HIP events on the
+kernels' stream brackets the K steps; ``value`` is their mean.  The roofline
+kernel is timed the same way: K back-to-back calls of it over the layers.
 
 Also reported (``also``): 1M-context decode (batch 4), with its scoring pass
 measured separately, and 8192-token chunked prefill onto a 57,344-token
@@ -33,132 +36,90 @@ METRIC = "MSA decode µs/layer-step & prefill tok/s at 60k/1M ctx; % HBM/MFMA pe
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="distinct layers (caches) cycled over by the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget for the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (PMC byte-counter calibration)")
+    ap.add_argument("--score-only", action="store_true",
+                    help="only run the headline's index_score_kernel calls (PMC passes)")
     return ap.parse_args()
 
 
-class Timer:
-    """Cold-cache, per-step HIP-event timing of an MsaStep (eager and graph)."""
+class HipEvent:
+    """A timing-only HIP event recorded on torch's current stream (created with
+    hipEventDisableSystemFence: no system-scope cache write-back/invalidate)."""
+    _hip = None
 
-    def __init__(self, step, flush_bytes=1 << 30):
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self):
+        import ctypes
         import torch
-        self.torch = torch
-        self.step = step
-        self.flush_buf = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
-        self.order = ["score", "topk"] + (["page_table"] if step.decode else []) + ["attend"]
-        self.calls = {"score": step.score, "topk": step.topk, "attend": step.attend,
-                      "page_table": getattr(step, "page_table_step", None)}
-        self.graph = None
+        rc = self._lib().hipEventRecord(self.ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
-    def _ev(self):
-        return self.torch.cuda.Event(enable_timing=True)
+    def elapsed_time(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
 
-    def flush(self):
-        # a read-only pass over 1 GiB evicts the step's inputs from the caches
-        # without leaving dirty lines whose write-back would slow the step
-        self.flush_sink = self.flush_buf.sum()
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
-    def eager_cold(self, steps, probe):
-        """Mean step ms and mean probe-call ms, each step after a cache flush."""
-        torch = self.torch
-        rec = []
-        torch.cuda.synchronize()
-        for _ in range(steps):
-            self.flush()
-            a, b, pa, pb = self._ev(), self._ev(), self._ev(), self._ev()
-            a.record()
-            for name in self.order:
-                if name == probe:
-                    pa.record()
-                    self.calls[name]()
-                    pb.record()
-                else:
-                    self.calls[name]()
-            b.record()
-            rec.append((a, b, pa, pb))
-        torch.cuda.synchronize()
-        step_ms = sum(a.elapsed_time(b) for a, b, _, _ in rec) / steps
-        probe_ms = sum(pa.elapsed_time(pb) for _, _, pa, pb in rec) / steps
-        return step_ms, probe_ms
 
-    def per_call_cold(self, reps):
-        torch = self.torch
-        out = {}
-        for name in self.order:
-            evs = []
-            for _ in range(reps):
-                self.flush()
-                a, b = self._ev(), self._ev()
-                # the calls before `name` run first so its inputs are current
-                for n2 in self.order:
-                    if n2 == name:
-                        a.record()
-                        self.calls[n2]()
-                        b.record()
-                        break
-                    self.calls[n2]()
-                evs.append((a, b))
-            torch.cuda.synchronize()
-            out[name] = sum(a.elapsed_time(b) for a, b in evs) / reps
-        return out
+def time_calls(fns, steps, warmup):
+    """Mean ms of `steps` calls cycling over fns, back to back, one event pair.
 
-    def capture(self):
-        torch = self.torch
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            self.step.run()  # warm the capture stream
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.step.run()
-        torch.cuda.synchronize()
-        self.graph = g
-        return g
+    The timed region is bracketed by torch.cuda.synchronize() on both sides.
+    """
+    import torch
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    a, b = HipEvent(), HipEvent()
+    a.record()
+    for i in range(steps):
+        fns[i % len(fns)]()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
-    def graph_cold(self, steps):
-        torch = self.torch
-        g = self.graph or self.capture()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        rec = []
-        for _ in range(steps):
-            self.flush()
-            a, b = self._ev(), self._ev()
-            a.record()
-            g.replay()
-            b.record()
-            rec.append((a, b))
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in rec) / steps
 
-    def graph_warm(self, steps):
-        torch = self.torch
-        g = self.graph or self.capture()
-        torch.cuda.synchronize()
-        a, b = self._ev(), self._ev()
-        a.record()
-        for _ in range(steps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
-
-    def eager_warm(self, steps):
-        torch = self.torch
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            self.step.run()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
+def make_layers(cfg, n, device="cuda"):
+    """n independent instances of the workload (layer l draws with seed + 1000*l)."""
+    import dataclasses
+    from block_sparse_attention_03_amd import inputs as gen
+    return [gen.make_inputs(dataclasses.replace(cfg, seed=cfg.seed + 1000 * l), device=device)
+            for l in range(n)]
 
 
 def cpu_baseline(cfg, x, budget_s):
@@ -194,6 +155,27 @@ def cpu_baseline(cfg, x, budget_s):
                       f"{el:.1f} s"}
 
 
+TRAFFIC_FILE = "profiles/index_score_decode_60k_traffic.json"
+
+
+def recorded_traffic():
+    """HBM bytes per launch of index_score_kernel on the headline workload, from
+    the FETCH_SIZE and WRITE_SIZE passes recorded in TRAFFIC_FILE -- or None if
+    the kernel's source has changed since they were taken."""
+    import hashlib
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, TRAFFIC_FILE)
+    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
 def roofline_entry(name, nbytes, ms, traffic=None):
     from block_sparse_attention_03_amd.accounting import HBM_PEAK_GBS
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -217,20 +199,33 @@ def main():
     from block_sparse_attention_03_amd.pipeline import MsaStep
     _lib.lib()  # fail loudly if the HIP library is missing
 
+    if args.copy_calibration:
+        # a plain copy of known size: each launch fetches and writes 256 MiB
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": a.numel() * 4, "launches": 4}))
+        return
+    if args.score_only:
+        cfg = gen.config(2)
+        four = [MsaStep(x) for x in make_layers(cfg, args.layers)]
+        ms = time_calls([s_.score for s_ in four], args.steps, args.warmup)
+        print(json.dumps({"index_score_ms": ms, "launches": args.steps + args.warmup}))
+        return
+
     # ---------------- headline: paged decode at 60k, batch 8 ----------------
     cfg = gen.config(2)
-    x = gen.make_inputs(cfg, device="cuda")
-    step = MsaStep(x)
-    tm = Timer(step)
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-    calls = tm.per_call_cold(10)
-    kernels = {"score": ("index_score_kernel", acc.score_bytes(cfg)),
-               "attend": ("decode_page_kernel + decode_merge_kernel", acc.decode_attn_bytes(cfg))}
-    probe = max(kernels, key=lambda k: calls[k])
-    eager_ms, probe_ms = tm.eager_cold(args.steps, probe)
-    graph_ms = tm.graph_cold(args.steps)
+    layers = make_layers(cfg, args.layers)
+    fused = [MsaStep(x, fused=True) for x in layers]   # msa_decode_step
+    four = [MsaStep(x) for x in layers]                # the four ABI calls
+    fused_ms = time_calls([s.run for s in fused], args.steps, args.warmup)
+    four_ms = time_calls([s.run for s in four], args.steps, args.warmup)
+    # roofline kernel: index_score_kernel, a single-kernel call (it and the
+    # page kernel each move about half of the step's bytes)
+    score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
+    attn_ms = time_calls([s.attend for s in four], args.steps, args.warmup)
     layer_bytes = acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
 
     def frac(ms_):
@@ -238,12 +233,12 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(graph_ms * 1e3, 2),
+        "value": round(fused_ms * 1e3, 2),
         "unit": "us/layer-step",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(graph_ms, 5),
+        "ms_per_step": round(fused_ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -253,60 +248,60 @@ def main():
                    "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
                    "num_idx_heads": cfg.num_idx_heads, "head_dim": cfg.head_dim,
                    "idx_dim": cfg.idx_dim, "block_size": cfg.block_size, "topk": cfg.topk,
-                   "seed": cfg.seed, "cache": "cold (1 GiB read pass before each step)",
-                   "launch": "HIP graph replay of the 4 ABI calls"},
-        "roofline": roofline_entry(kernels[probe][0], kernels[probe][1], probe_ms),
+                   "seed": cfg.seed, "layers": args.layers,
+                   "timing": "layer-steps back to back over distinct per-layer caches (cold HBM)",
+                   "entry_point": "msa_decode_step"},
+        "roofline": roofline_entry("index_score_kernel", acc.score_bytes(cfg), score_ms,
+                                   recorded_traffic()),
         "layer_step": {"algorithmic_bytes": layer_bytes,
-                       "hbm_frac_graph_cold": frac(graph_ms),
-                       "us_eager_cold": round(eager_ms * 1e3, 2), "hbm_frac_eager_cold": frac(eager_ms),
-                       "us_graph_warm": round(tm.graph_warm(args.steps) * 1e3, 2),
-                       "us_eager_warm": round(tm.eager_warm(args.steps) * 1e3, 2),
-                       "per_call_us_cold": {k: round(v * 1e3, 2) for k, v in calls.items()}},
+                       "hbm_frac": frac(fused_ms),
+                       "us_four_calls": round(four_ms * 1e3, 2),
+                       "hbm_frac_four_calls": frac(four_ms),
+                       "decode_attention_call": roofline_entry(
+                           "decode_page_kernel + decode_merge_kernel", acc.decode_attn_bytes(cfg),
+                           attn_ms)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
-    del tm, step, x
+        result["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds)
+    del fused, four, layers
     torch.cuda.empty_cache()
 
     if not args.no_also:
         also = {}
-        # 1M-context decode, batch 4: scoring pass reported on its own
+        # 1M-context decode, batch 4 (18 GB of K/V per layer): 2 layers
         c4 = gen.config(4)
-        x4 = gen.make_inputs(c4, device="cuda")
-        s4 = MsaStep(x4)
-        t4 = Timer(s4)
-        s4.run()
-        n4 = max(10, args.steps // 4)
-        eager4, score4 = t4.eager_cold(n4, "score")
-        graph4 = t4.graph_cold(n4)
+        l4 = make_layers(c4, 2)
+        f4 = [MsaStep(x, fused=True) for x in l4]
+        s4 = [MsaStep(x) for x in l4]
+        n4 = max(10, args.steps // 8)
+        ms4 = time_calls([s.run for s in f4], n4, 2)
+        score4 = time_calls([s.score for s in s4], n4, 2)
         b4 = acc.score_bytes(c4) + acc.decode_attn_bytes(c4)
-        also[c4.name] = {"us_per_layer_step": round(graph4 * 1e3, 2),
-                         "layer_step_hbm_frac": round(b4 / (graph4 * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
-                         "us_eager_cold": round(eager4 * 1e3, 2),
-                         "scoring_pass": roofline_entry("index_score_kernel", acc.score_bytes(c4), score4),
-                         "per_call_us_cold": {k: round(v * 1e3, 2) for k, v in t4.per_call_cold(3).items()}}
-        del t4, s4, x4
+        also[c4.name] = {"us_per_layer_step": round(ms4 * 1e3, 2),
+                         "layer_step_hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
+                         "us_four_calls": round(time_calls([s.run for s in s4], n4, 2) * 1e3, 2),
+                         "scoring_pass": roofline_entry("index_score_kernel", acc.score_bytes(c4), score4)}
+        del f4, s4, l4
         torch.cuda.empty_cache()
-        # chunked prefill: 8192 new tokens on a 57,344-token prefix
+        # chunked prefill: 8192 new tokens on a 57,344-token prefix, 2 layers
         c3 = gen.config(3)
-        x3 = gen.make_inputs(c3, device="cuda")
-        s3 = MsaStep(x3)
-        t3 = Timer(s3)
-        s3.run()
-        n3 = max(5, args.steps // 20)
-        eager3, attn3 = t3.eager_cold(n3, "attend")
-        graph3 = t3.graph_cold(n3)
-        calls3 = t3.per_call_cold(3)
+        l3 = make_layers(c3, 2)
+        s3 = [MsaStep(x) for x in l3]
+        n3 = max(6, args.steps // 25)
+        ms3 = time_calls([s.run for s in s3], n3, 2)
+        score3 = time_calls([s.score for s in s3], n3, 2)
+        attn3 = time_calls([s.attend for s in s3], n3, 2)
         fl_attn, fl_score = acc.attn_flops(c3), acc.score_flops(c3)
         tf = lambda fl, ms_: fl / (ms_ * 1e-3) / 1e12
         also[c3.name] = {
-            "tokens_per_s": round(c3.total_q / (graph3 * 1e-3), 1),
-            "ms_per_step": round(graph3, 4), "ms_eager_cold": round(eager3, 4),
+            "tokens_per_s": round(c3.total_q / (ms3 * 1e-3), 1),
+            "ms_per_step": round(ms3, 4),
+            "sparse_attn_call_ms": round(attn3, 4),
             "sparse_attn_call_mfma_frac": round(tf(fl_attn, attn3) / acc.BF16_PEAK_TFLOPS, 4),
-            "index_score_mfma_frac": round(tf(fl_score, calls3["score"]) / acc.BF16_PEAK_TFLOPS, 4),
-            "attn_flops": fl_attn, "score_flops": fl_score,
-            "per_call_us_cold": {k: round(v * 1e3, 2) for k, v in calls3.items()}}
-        del t3, s3, x3
+            "index_score_ms": round(score3, 4),
+            "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
+            "attn_flops": fl_attn, "score_flops": fl_score}
+        del s3, l3
         torch.cuda.empty_cache()
         result["also"] = also
 

@@ -18,7 +18,7 @@
 // the LDS transpose read.  Each page leaves a normalised partial
 // output and its log-sum-exp in the workspace; a second kernel merges a row's
 // pages with the Log-Sum-Exp rule (aivizor, KV-Block-Major paragraph).
-#include "msa_common.hpp"
+#include "select.hpp"
 
 namespace msa {
 namespace {
@@ -42,31 +42,25 @@ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
     return w;
 }
 
-__global__ __launch_bounds__(kDecThreads)
-void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
-                        const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
-                        const uint16_t* __restrict__ v_cache,
-                        const int32_t* __restrict__ page_table,  // [R, k]
-                        const int32_t* __restrict__ row_lens,    // [R]
-                        void* __restrict__ ws, int Hq, int Hkv, int R, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kVsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[kMaxGroup * kPStride];
-    __shared__ float red_max[4][kMaxGroup];
-    __shared__ float red_sum[4][kMaxGroup];
+struct DecodeShared {
+    uint16_t vs[kBlock * kVsStride];
+    uint16_t pl[kMaxGroup * kPStride];
+    float red_max[4][kMaxGroup];
+    float red_sum[4][kMaxGroup];
+};
 
-    const int slot = blockIdx.x;
-    const int r = blockIdx.y;
-    const int n_tok = row_lens[r];
-    if (slot * kBlock >= n_tok) return;  // page not used by this row (uniform)
-    const int nv = min(kBlock, n_tok - slot * kBlock);
-    const int G = Hq / Hkv;
-    const int s = r / Hkv;
-    const int g = r % Hkv;
-    const int page = page_table[(size_t)r * kTopK + slot];
-    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
-    const uint16_t* kp = k_cache + page_off;
-    const uint16_t* vp = v_cache + page_off;
-
+// The G query heads of row r (sequence s, group g) against one page holding
+// nv valid tokens: writes the normalised partial output and log-sum-exp of
+// page slot `slot`.  Every thread of the 256-thread workgroup calls it.
+__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ kp,
+                                            const uint16_t* __restrict__ vp, int nv, int s, int g,
+                                            int G, int Hq, int r, int slot, void* __restrict__ ws,
+                                            int R, float scale_log2, DecodeShared& sh) {
+    uint16_t* vs = sh.vs;
+    uint16_t* pl = sh.pl;
+    auto& red_max = sh.red_max;
+    auto& red_sum = sh.red_sum;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
@@ -182,6 +176,78 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
     }
 }
 
+
+__global__ __launch_bounds__(kDecThreads)
+void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
+                        const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                        const uint16_t* __restrict__ v_cache,
+                        const int32_t* __restrict__ page_table,  // [R, k]
+                        const int32_t* __restrict__ row_lens,    // [R]
+                        void* __restrict__ ws, int Hq, int Hkv, int R, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    const int slot = blockIdx.x;
+    const int r = blockIdx.y;
+    const int n_tok = row_lens[r];
+    if (slot * kBlock >= n_tok) return;  // page not used by this row (uniform)
+    const int nv = min(kBlock, n_tok - slot * kBlock);
+    const int G = Hq / Hkv;
+    const int s = r / Hkv;
+    const int g = r % Hkv;
+    const int page = page_table[(size_t)r * kTopK + slot];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, G, Hq, r, slot, ws, R,
+                scale_log2, sh);
+}
+
+// Fused decode: the workgroup of (row r = s*H_kv + g, slot i) selects the
+// row's top-k blocks itself from the block scores (every workgroup of the row
+// makes the same, deterministic selection), maps its i-th selected block to
+// a physical page through the block table -- the row's page table, kept on
+// chip -- and attends that page.  Slot 0 also publishes the row's selection
+// and length.
+template <int NPT, int W>
+__global__ __launch_bounds__(kDecThreads)
+void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxblk]
+                         const int32_t* __restrict__ block_table,
+                         const int32_t* __restrict__ seq_lens,
+                         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                         const uint16_t* __restrict__ v_cache, int32_t* __restrict__ row_lens,
+                         int32_t* __restrict__ sel_out, void* __restrict__ ws, int Hq, int Hkv,
+                         int R, int maxblk, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    __shared__ SelectScratch<W> ssh;
+    __shared__ int32_t sel_lds[kTopK];
+    const int slot = blockIdx.x;
+    const int r = blockIdx.y;
+    const int s = r / Hkv;
+    const int g = r % Hkv;
+    const int p = seq_lens[s] - 1;
+    const int b_loc = p / kBlock;
+    const int n_sel = min(kTopK, b_loc + 1);
+    if (slot >= n_sel) return;  // uniform
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    // W = 1: wavefront 0 selects alone (no barriers inside the search) while
+    // the others wait; W = 4: all four wavefronts share a long row
+    if (W == 4 || wave == 0) {
+        float raw[NPT];
+        load_candidates<NPT, W>(scores + (size_t)r * maxblk, maxblk, W == 1 ? 0 : wave, lane, raw);
+        select_row<NPT, W>(raw, b_loc, W == 1 ? 0 : wave, lane, &ssh, sel_lds);
+    }
+    __syncthreads();
+    const int b = sel_lds[slot];
+    if (slot == 0) {
+        if (threadIdx.x < kTopK && sel_out) sel_out[(size_t)r * kTopK + threadIdx.x] = sel_lds[threadIdx.x];
+        if (threadIdx.x == 0) row_lens[r] = (n_sel - 1) * kBlock + (p - kBlock * b_loc + 1);
+    }
+    // ascending order puts the own (partial) block last
+    const int nv = (slot == n_sel - 1) ? p - kBlock * b_loc + 1 : kBlock;
+    const int page = block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, Hq / Hkv, Hq, r, slot, ws, R,
+                scale_log2, sh);
+}
+
 // One thread per (row, head, dim): Log-Sum-Exp merge of the row's pages.
 __global__ __launch_bounds__(kHeadDim)
 void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __restrict__ ws,
@@ -244,5 +310,59 @@ hipError_t msa_launch_decode(const MsaShape& s, const uint16_t* q, const uint16_
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(R * G), dim3(kHeadDim), 0, st, row_lens, ws, out,
                        lse, s.Hq, s.Hkv, R);
+    return hipGetLastError();
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t msa_decode_step_ws_bytes(const MsaShape& s) {
+    const size_t R = (size_t)s.B * s.Hkv;
+    return msa_decode_ws_bytes(s) + align256(R * s.maxblk * sizeof(float)) +
+           align256(R * sizeof(int32_t));
+}
+
+template <int NPT, int W>
+static hipError_t launch_fused(const MsaShape& s, const float* scores, const int32_t* block_table,
+                               const int32_t* seq_lens, const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, int32_t* row_lens, int32_t* sel_out,
+                               void* ws, hipStream_t st) {
+    using namespace msa;
+    const int R = s.B * s.Hkv;
+    hipLaunchKernelGGL((decode_fused_kernel<NPT, W>), dim3(kTopK, R), dim3(kDecThreads), 0, st,
+                       scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws,
+                       s.Hq, s.Hkv, R, s.maxblk, s.scale * kLog2e);
+    return hipGetLastError();
+}
+
+hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, const uint16_t* kidx,
+                                  const uint16_t* q, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, uint16_t* out, float* lse,
+                                  int32_t* sel_out, void* ws, hipStream_t st) {
+    using namespace msa;
+    const int R = s.B * s.Hkv;
+    if (R == 0) return hipSuccess;
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base + msa_decode_ws_bytes(s));
+    int32_t* row_lens = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scores) +
+                                                   align256((size_t)R * s.maxblk * sizeof(float)));
+    hipError_t e = msa_launch_index_score_decode(s, q_idx, kidx, block_table, seq_lens, scores, st);
+    if (e != hipSuccess) return e;
+    const int m = s.maxblk;
+#define MSA_FUSED(NPT, W) \
+    launch_fused<NPT, W>(s, scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws, st)
+    if (m <= 4 * kWave) e = MSA_FUSED(4, 1);
+    else if (m <= 8 * kWave) e = MSA_FUSED(8, 1);
+    else if (m <= 16 * kWave) e = MSA_FUSED(16, 1);
+    else if (m <= 8 * kDecThreads) e = MSA_FUSED(8, 4);
+    else if (m <= 16 * kDecThreads) e = MSA_FUSED(16, 4);
+    else if (m <= 32 * kDecThreads) e = MSA_FUSED(32, 4);
+    else e = MSA_FUSED(64, 4);
+#undef MSA_FUSED
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(R * (s.Hq / s.Hkv)), dim3(kHeadDim), 0, st,
+                       row_lens, ws, out, lse, s.Hq, s.Hkv, R);
     return hipGetLastError();
 }

@@ -49,8 +49,9 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     if (b >= maxblk) return;
 
     const int L = seq_lens[s];
-    const int q0 = cu_q[s];
-    const int nq = cu_q[s + 1] - q0;
+    // cu_q == nullptr: decode, query token s is sequence s's only query
+    const int q0 = cu_q ? cu_q[s] : s;
+    const int nq = cu_q ? cu_q[s + 1] - q0 : 1;
     if (nq <= 0) return;
     const int R = (Hidx == 1) ? Hkv : 1;  // rows per query served by this index head
     const int nrows = nq * R;
@@ -335,5 +336,17 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
     hipLaunchKernelGGL(index_score_kernel, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
                        block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk);
+    return hipGetLastError();
+}
+
+hipError_t msa_launch_index_score_decode(const MsaShape& s, const uint16_t* q_idx,
+                                         const uint16_t* kidx, const int32_t* block_table,
+                                         const int32_t* seq_lens, float* scores, hipStream_t st) {
+    using namespace msa;
+    if (s.B == 0) return hipSuccess;
+    dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
+    hipLaunchKernelGGL(index_score_kernel, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
+                       block_table, seq_lens, static_cast<const int32_t*>(nullptr), scores, s.Hkv,
+                       s.Hidx, s.maxblk);
     return hipGetLastError();
 }

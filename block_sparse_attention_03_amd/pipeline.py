@@ -1,7 +1,7 @@
 """One MSA layer-step through the C ABI, with its device buffers.
 
 Decode:  msa_index_score -> msa_topk_blocks -> msa_build_page_table ->
-         msa_sparse_attn_decode.
+         msa_sparse_attn_decode, or the fused msa_decode_step (same results).
 Prefill: msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill.
 This module only allocates the outputs and the workspace (torch device memory)
 and calls the library; every step of the computation runs in its kernels.
@@ -14,7 +14,7 @@ from . import _lib as L
 
 
 class MsaStep:
-    def __init__(self, x, lse: bool = True):
+    def __init__(self, x, lse: bool = True, fused: bool = False):
         cfg = x.cfg
         self.x = x
         self.cfg = cfg
@@ -26,7 +26,10 @@ class MsaStep:
         self.sel = torch.empty((T, H, cfg.topk), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, cfg.num_q_heads), dtype=torch.float32, device=dev) if lse else None
-        if self.decode:
+        self.fused = fused and self.decode
+        if self.fused:
+            nbytes = L.msa_decode_step_workspace_size(self.dims)
+        elif self.decode:
             R = cfg.num_seqs * H
             self.page_table = torch.empty((R, cfg.topk), dtype=torch.int32, device=dev)
             self.row_lens = torch.empty((R,), dtype=torch.int32, device=dev)
@@ -62,7 +65,16 @@ class MsaStep:
                                       x.block_table, x.seq_lens, x.cu_q, self.sel, self.out,
                                       self.lse, self.workspace, stream)
 
+    def fused_step(self, stream=None):
+        x = self.x
+        L.msa_decode_step(self.dims, x.q_idx, x.kidx_cache, x.q, x.k_cache, x.v_cache,
+                          x.block_table, x.seq_lens, self.out, self.lse, self.sel, self.workspace,
+                          stream)
+
     def run(self, stream=None):
+        if self.fused:
+            self.fused_step(stream)
+            return self.out
         self.score(stream)
         self.topk(stream)
         if self.decode:

@@ -171,9 +171,33 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t total_q, co
                                      float *lse, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/*
+ * The whole decode layer-step in three launches (the fused form of the four
+ * calls above; same results, bit for bit).  Scoring runs as in
+ * msa_index_score; then every (row r = s*H_kv + g, page slot i) workgroup
+ * makes the row's top-k selection itself from the block scores -- the same
+ * deterministic rule as msa_topk_blocks -- maps its i-th selected block to a
+ * physical page through block_table (the row's page table, built on chip:
+ * [aivizor] paragraph on MSA with paged attention) and attends that page as
+ * msa_sparse_attn_decode does; a final kernel merges each row's pages with
+ * the Log-Sum-Exp rule.  One query per sequence (decode, p = seq_lens[s]-1).
+ *   q_idx [B, H_kv, 64], q [B, H_q, 128]; caches, block_table, seq_lens as above
+ *   out   [B, H_q, 128] bf16 (output); lse [B, H_q] fp32 or NULL
+ *   sel   [B, H_kv, k] int32 (output, the selection) or NULL
+ *   workspace: at least msa_decode_step_workspace_size(dims) bytes, 256-byte
+ *   aligned; no initial contents required.
+ */
+msa_status_t msa_decode_step(const msa_dims_t *dims, const uint16_t *q_idx,
+                             const uint16_t *kidx_cache, const uint16_t *q,
+                             const uint16_t *k_cache, const uint16_t *v_cache,
+                             const int32_t *block_table, const int32_t *seq_lens, uint16_t *out,
+                             float *lse, int32_t *sel, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* Workspace sizes in bytes (0 for invalid dims). */
 size_t msa_decode_workspace_size(const msa_dims_t *dims);
 size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);
+size_t msa_decode_step_workspace_size(const msa_dims_t *dims);
 
 /* Static, human-readable name of a status code. */
 const char *msa_status_string(msa_status_t status);

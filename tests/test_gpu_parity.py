@@ -162,3 +162,28 @@ def test_graph_replay_matches_eager(prefill):
         assert torch.equal(step.out, ref_out), f"replay {i}: out differs"
         assert torch.equal(step.lse, ref_lse), f"replay {i}: lse differs"
         assert torch.equal(step.sel, ref_sel), f"replay {i}: sel differs"
+
+
+@pytest.mark.parametrize("cfg", [
+    SMALL[0], SMALL[1], SMALL[3],
+    gen.MsaConfig("fused_hidx", [7000, 300], [1, 1], 12, 3, num_idx_heads=3, permute_pages=True,
+                  seed=43),
+    gen.config(2), gen.config(5), gen.config(4),
+], ids=lambda c: c.name)
+def test_fused_decode_step_equals_the_four_calls(cfg):
+    """msa_decode_step makes the same selection and the same page products as
+    msa_index_score -> msa_topk_blocks -> msa_build_page_table ->
+    msa_sparse_attn_decode: out, lse and sel are bit-identical."""
+    print(f"[fused] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    ref = MsaStep(x)
+    ref.run()
+    fused = MsaStep(x, fused=True)
+    fused.sel.fill_(-7)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.sel, ref.sel)
+    assert torch.equal(fused.out, ref.out)
+    assert torch.equal(fused.lse, ref.lse)
+    if cfg.total_q * cfg.num_q_heads <= 4096:
+        parity.check_attention(cfg, x, fused)
