@@ -187,3 +187,25 @@ def test_fused_decode_step_equals_the_four_calls(cfg):
     assert torch.equal(fused.lse, ref.lse)
     if cfg.total_q * cfg.num_q_heads <= 4096:
         parity.check_attention(cfg, x, fused)
+
+
+def test_fused_decode_step_repeats_and_long_rows():
+    """msa_decode_step called again and again on one workspace, on short rows
+    (one selecting wavefront per page workgroup) and on rows over 1024 blocks
+    (four selecting wavefronts): each call equals the four-call result."""
+    for cfg in (gen.MsaConfig("step_repeat", [9000, 3000, 700], [1, 1, 1], 12, 3,
+                              permute_pages=True, seed=44),
+                gen.MsaConfig("step_long_rows", [140000, 9000], [1, 1], 8, 2,
+                              permute_pages=True, seed=45)):
+        print(f"[fused-repeat] {cfg.name} maxblk={cfg.max_blocks}", flush=True)
+        x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+        ref = MsaStep(x)
+        ref.run()
+        fused = MsaStep(x, fused=True)
+        for i in range(5):
+            fused.out.zero_()
+            fused.run()
+            torch.cuda.synchronize()
+            assert torch.equal(fused.out, ref.out), f"{cfg.name} call {i}"
+            assert torch.equal(fused.lse, ref.lse), f"{cfg.name} call {i}"
+            assert torch.equal(fused.sel, ref.sel), f"{cfg.name} call {i}"
