@@ -13,7 +13,7 @@
 // (S^T = K Q^T, fp32 accumulate); the page's per-head max and sum are
 // combined through LDS; P is rounded to bf16 and shared through LDS; then
 // wavefront w forms dims 32w..32w+31 of O^T = V^T P^T.  V is loaded with
-// fully coalesced 16-byte reads into a row-major LDS tile, and the transposed
+// fully coalesced 16-byte reads into a row-major (swizzled) LDS tile, and the transposed
 // matrix-core operand (4 consecutive tokens of one dim per lane) comes from
 // the LDS transpose read.  Each page leaves a normalised partial
 // output and its log-sum-exp in the workspace; a second kernel merges a row's
@@ -24,8 +24,14 @@ namespace msa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kVsStride = kHeadDim + 32; // bf16 per V row in LDS (tokens x dims); 320 B keeps the
-                                         // transpose reads of 4 rows x 64 B on distinct banks
+// V sits in LDS as 128 rows (tokens) of 256 B, unpadded; the 16-byte chunk c
+// of token t is stored at chunk c ^ 2(t mod 8).  A transpose read takes the
+// same 32 B of 16 consecutive tokens, and the swizzle puts any 8 consecutive
+// tokens' copies of those 32 B on 8 disjoint sets of 8 banks, so the reads are
+// conflict-free; with no padding, four workgroups fit in a compute unit.
+__device__ __forceinline__ int vs_off(int t, int d) {  // bf16 offset of (token t, dim d)
+    return t * kHeadDim + ((((d >> 3) ^ ((t & 7) << 1))) << 3) + (d & 7);
+}
 constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -43,7 +49,7 @@ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
 }
 
 struct DecodeShared {
-    uint16_t vs[kBlock * kVsStride];
+    uint16_t vs[kBlock * kHeadDim];
     uint16_t pl[kMaxGroup * kPStride];
     float red_max[4][kMaxGroup];
     float red_sum[4][kMaxGroup];
@@ -93,7 +99,7 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
 
 #pragma unroll
         for (int it = 0; it < 8; ++it)
-            *reinterpret_cast<u32x4*>(vs + (tid / 16 + 16 * it) * kVsStride + 8 * (tid % 16)) = vv[it];
+            *reinterpret_cast<u32x4*>(vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
 
         // S^T = K Q^T for tokens 32w + 16j + 4kg + rr, head n
         f32x4 sacc[2];
@@ -153,9 +159,9 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
             for (int mt = 0; mt < 2; ++mt) {
                 // lane j of group kg points at token 32ks + 4kg + j/4 (and +16),
                 // dims d0 + 4(j%4); the transpose read hands lane i dim d0 + i
-                const uint16_t* src = vs + (ta + n / 4) * kVsStride + 32 * wave + 16 * mt + 4 * (n % 4);
+                const uint16_t* src = vs + vs_off(ta + n / 4, 32 * wave + 16 * mt + 4 * (n % 4));
                 const u32x2 v0a = lds_read_tr16(src);
-                const u32x2 v1a = lds_read_tr16(src + 16 * kVsStride);
+                const u32x2 v1a = lds_read_tr16(src + 16 * kHeadDim);  // token + 16: same swizzle
                 oacc[mt] = mfma16(as_bf16x8(u32x4{v0a[0], v0a[1], v1a[0], v1a[1]}), pbv, oacc[mt]);
             }
         }
@@ -204,8 +210,9 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
 // makes the same, deterministic selection), maps its i-th selected block to
 // a physical page through the block table -- the row's page table, kept on
 // chip -- and attends that page.  Slot 0 also publishes the row's selection
-// and length.
-template <int NPT, int W>
+// and length.  With PAGES the block-table entries are loaded beside the
+// scores, so the selection hands over pages directly.
+template <int NPT, int W, bool PAGES>
 __global__ __launch_bounds__(kDecThreads)
 void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxblk]
                          const int32_t* __restrict__ block_table,
@@ -215,35 +222,47 @@ void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
                          int32_t* __restrict__ sel_out, void* __restrict__ ws, int Hq, int Hkv,
                          int R, int maxblk, float scale_log2) {
     __shared__ __attribute__((aligned(16))) DecodeShared sh;
-    __shared__ SelectScratch<W> ssh;
-    __shared__ int32_t sel_lds[kTopK];
+    __shared__ int32_t sel_idx[kTopK];
+    __shared__ int32_t sel_page[kTopK];
+    // the selection's LDS lives in the V tile, which is written only after
+    // the barrier that ends the selection
+    static_assert(sizeof(SelectShared<W>) <= sizeof(sh.vs), "selection scratch");
+    SelectShared<W>* ssh = reinterpret_cast<SelectShared<W>*>(sh.vs);
     const int slot = blockIdx.x;
     const int r = blockIdx.y;
     const int s = r / Hkv;
     const int g = r % Hkv;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int w = (W == 1) ? 0 : wave;
+    // W = 1: wavefront 0 selects alone (no barriers inside the search) while
+    // the others wait; W = 4: all four wavefronts share a long row.  The
+    // candidate loads are issued before the sequence length arrives.
+    const bool selecting = (W == 4 || wave == 0);
+    float raw[NPT];
+    int page[NPT];
+    if (selecting)
+        load_candidates<NPT, W, PAGES>(scores + (size_t)r * maxblk, block_table + (size_t)s * maxblk,
+                                       maxblk, w, lane, raw, page);
     const int p = seq_lens[s] - 1;
     const int b_loc = p / kBlock;
     const int n_sel = min(kTopK, b_loc + 1);
-    if (slot >= n_sel) return;  // uniform
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    // W = 1: wavefront 0 selects alone (no barriers inside the search) while
-    // the others wait; W = 4: all four wavefronts share a long row
-    if (W == 4 || wave == 0) {
-        float raw[NPT];
-        load_candidates<NPT, W>(scores + (size_t)r * maxblk, maxblk, W == 1 ? 0 : wave, lane, raw);
-        select_row<NPT, W>(raw, b_loc, W == 1 ? 0 : wave, lane, &ssh, sel_lds);
-    }
+    if (selecting)
+        select_row<NPT, W>(raw, page, b_loc, w, lane, ssh, [&](int pos, uint32_t, int b, int pg) {
+            sel_idx[pos] = b;
+            sel_page[pos] = pg;
+        });
     __syncthreads();
-    const int b = sel_lds[slot];
+    if (slot >= n_sel) return;  // uniform
+    const int b = sel_idx[slot];
     if (slot == 0) {
-        if (threadIdx.x < kTopK && sel_out) sel_out[(size_t)r * kTopK + threadIdx.x] = sel_lds[threadIdx.x];
+        if (threadIdx.x < kTopK && sel_out) sel_out[(size_t)r * kTopK + threadIdx.x] = sel_idx[threadIdx.x];
         if (threadIdx.x == 0) row_lens[r] = (n_sel - 1) * kBlock + (p - kBlock * b_loc + 1);
     }
     // ascending order puts the own (partial) block last
     const int nv = (slot == n_sel - 1) ? p - kBlock * b_loc + 1 : kBlock;
-    const int page = block_table[(size_t)s * maxblk + b];
-    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    const int pg = PAGES ? sel_page[slot] : block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)pg * Hkv + g) * kBlock * kHeadDim;
     attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, Hq / Hkv, Hq, r, slot, ws, R,
                 scale_log2, sh);
 }
@@ -317,20 +336,28 @@ namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
+// Rows longer than this many blocks select in the standalone kernel (one
+// 1024-thread workgroup per row) rather than inside the page workgroups.
+constexpr int kFusedMaxBlocks = 32 * msa::kDecThreads;
+
+// Workspace of the decode step: page partials, block scores, row lengths and,
+// for rows past kFusedMaxBlocks, the selection and page table.
 size_t msa_decode_step_ws_bytes(const MsaShape& s) {
     const size_t R = (size_t)s.B * s.Hkv;
-    return msa_decode_ws_bytes(s) + align256(R * s.maxblk * sizeof(float)) +
-           align256(R * sizeof(int32_t));
+    size_t bytes = msa_decode_ws_bytes(s) + align256(R * s.maxblk * sizeof(float)) +
+                   align256(R * sizeof(int32_t));
+    if (s.maxblk > kFusedMaxBlocks) bytes += 2 * align256(R * msa::kTopK * sizeof(int32_t));
+    return bytes;
 }
 
-template <int NPT, int W>
+template <int NPT, int W, bool PAGES>
 static hipError_t launch_fused(const MsaShape& s, const float* scores, const int32_t* block_table,
                                const int32_t* seq_lens, const uint16_t* q, const uint16_t* k_cache,
                                const uint16_t* v_cache, int32_t* row_lens, int32_t* sel_out,
                                void* ws, hipStream_t st) {
     using namespace msa;
     const int R = s.B * s.Hkv;
-    hipLaunchKernelGGL((decode_fused_kernel<NPT, W>), dim3(kTopK, R), dim3(kDecThreads), 0, st,
+    hipLaunchKernelGGL((decode_fused_kernel<NPT, W, PAGES>), dim3(kTopK, R), dim3(kDecThreads), 0, st,
                        scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws,
                        s.Hq, s.Hkv, R, s.maxblk, s.scale * kLog2e);
     return hipGetLastError();
@@ -351,15 +378,25 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
     hipError_t e = msa_launch_index_score_decode(s, q_idx, kidx, block_table, seq_lens, scores, st);
     if (e != hipSuccess) return e;
     const int m = s.maxblk;
-#define MSA_FUSED(NPT, W) \
-    launch_fused<NPT, W>(s, scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws, st)
-    if (m <= 4 * kWave) e = MSA_FUSED(4, 1);
-    else if (m <= 8 * kWave) e = MSA_FUSED(8, 1);
-    else if (m <= 16 * kWave) e = MSA_FUSED(16, 1);
-    else if (m <= 8 * kDecThreads) e = MSA_FUSED(8, 4);
-    else if (m <= 16 * kDecThreads) e = MSA_FUSED(16, 4);
-    else if (m <= 32 * kDecThreads) e = MSA_FUSED(32, 4);
-    else e = MSA_FUSED(64, 4);
+    if (m > kFusedMaxBlocks) {
+        char* extra = reinterpret_cast<char*>(row_lens) + align256((size_t)R * sizeof(int32_t));
+        int32_t* page_table = reinterpret_cast<int32_t*>(extra);
+        int32_t* sel = sel_out ? sel_out
+                               : reinterpret_cast<int32_t*>(extra + align256((size_t)R * kTopK * sizeof(int32_t)));
+        e = msa_launch_topk(s, s.B, scores, seq_lens, nullptr, sel, st);
+        if (e != hipSuccess) return e;
+        e = msa_launch_page_table(s, sel, block_table, seq_lens, page_table, row_lens, st);
+        if (e != hipSuccess) return e;
+        return msa_launch_decode(s, q, k_cache, v_cache, page_table, row_lens, out, lse, ws, st);
+    }
+#define MSA_FUSED(NPT, W, PAGES) \
+    launch_fused<NPT, W, PAGES>(s, scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws, st)
+    if (m <= 4 * kWave) e = MSA_FUSED(4, 1, true);
+    else if (m <= 8 * kWave) e = MSA_FUSED(8, 1, true);
+    else if (m <= 16 * kWave) e = MSA_FUSED(16, 1, true);
+    else if (m <= 8 * kDecThreads) e = MSA_FUSED(8, 4, true);
+    else if (m <= 16 * kDecThreads) e = MSA_FUSED(16, 4, true);
+    else e = MSA_FUSED(32, 4, false);
 #undef MSA_FUSED
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(R * (s.Hq / s.Hkv)), dim3(kHeadDim), 0, st,

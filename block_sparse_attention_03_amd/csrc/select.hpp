@@ -8,13 +8,29 @@
 //
 // Method.  Each candidate becomes a 32-bit key whose unsigned order is the
 // float order of its score (-0.0 folded into +0.0); the own block gets the
-// largest key.  The kk-th largest key (kk = min(k, b_loc+1)) is found by a
-// 32-step bitwise search whose counts are wavefront ballot popcounts.  Keys
-// above it are kept; among keys equal to it the lowest blocks fill the rest.
-// Candidates are dealt to lanes interleaved (block = slot*64 + lane), so the
-// score loads are coalesced and ascending block order is (slot, lane) order: output positions are ballot prefix counts.  Long rows are
-// split over W wavefronts, each selecting its range's top-k, and one
-// wavefront then selects from the survivors.
+// largest key and an empty slot the key 0.  Candidates are dealt to lanes
+// interleaved (block = base + slot*64 + lane), so score loads are coalesced and
+// ascending block order is (slot, lane) order.
+//
+// The kk-th largest key (kk = min(k, #candidates)) comes from a bitwise
+// search whose counts are wavefront ballot popcounts.  On this hardware one
+// step costs a vector compare per register, each followed by a scalar
+// popcount of its lane mask, so the search is run on as few registers as
+// possible:
+//   1. each lane takes the largest of its keys; the kk-th largest of these 64
+//      lane maxima, T0, is at most the kk-th largest key (kk distinct lanes
+//      hold a key >= T0), so every key of the selection is >= T0;
+//   2. the keys >= T0 (usually a few more than kk) are compacted, in
+//      ascending block order, one per lane through LDS;
+//   3. the search runs again on that single register.
+// When more than 64 keys are >= T0 (heavy ties) the search runs on all keys.
+// Each search stops early once exactly kk keys are >= the candidate
+// threshold: those keys are then the selection.  Keys above the threshold are
+// kept; among keys equal to it the lowest blocks fill the rest.
+//
+// Long rows are split over W wavefronts, each selecting its range's top-k;
+// wavefront 0 then selects from the W*k survivors, which already sit in
+// ascending block order, so the same rule and tie-break apply.
 #pragma once
 
 #include "msa_common.hpp"
@@ -54,116 +70,198 @@ __device__ __forceinline__ SeqInfo lookup_seq(const int32_t* __restrict__ cu_q,
     }
 }
 
-// Wave-level selection.  Candidates sit at positions i*64 + lane (i < NPT) in
-// ascending block order; idx[i] < 0 marks an empty position.  Keeps
-// min(k, #candidates) of them -- the own block b_loc first, then higher score,
-// then lower block -- and writes their block indices in ascending order to
-// out[0..] (and their scores to out_score if given), then -1 up to k.
+// A candidate in LDS: ordered key, block index and physical page.
+struct alignas(16) Cand {
+    uint32_t key;
+    int32_t idx;
+    int32_t page;
+    int32_t pad;
+};
+
+// Largest T with #{key >= T} >= kk, or an earlier T with #{key >= T} == kk.
+// Either way the keys > T, then the lowest-block keys == T up to kk in all,
+// are the kk largest keys with ties to the lower block.  Needs
+// 1 <= kk <= #{key >= 1}.
 template <int NPT>
-__device__ void select_wave(const int (&idx)[NPT], const float (&raw)[NPT], int b_loc, int lane,
-                            int32_t* out, float* out_score) {
-    uint32_t key[NPT];
-    int n = 0;
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[NPT], int kk) {
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        key[i] = idx[i] < 0 ? 0u : (idx[i] == b_loc ? 0xFFFFFFFFu : order_key(raw[i]));
-        n += __popcll(__ballot(idx[i] >= 0));
-    }
-    const int kk = n < kTopK ? n : kTopK;
-    uint32_t T = 1u;  // every candidate's key is >= 1 (order_key(-inf) = 0x007FFFFF)
-    if (n > kTopK) {
-        // kk-th largest key: the largest T with #{key >= T} >= kk.
-        T = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int i = 0; i < NPT; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-            if (cnt >= kk) T = cand;
+        for (int i = 0; i < NPT; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+        if (cnt >= kk) {
+            T = cand;
+            if (cnt == kk) break;
         }
     }
+    return T;
+}
+
+// Writes the kept candidates (threshold T, see kth_key) in ascending block
+// order through out(pos, key, idx_of(i), page_of(i)), then out(pos, 0, -1, -1)
+// for the positions kk .. k-1.  idx_of / page_of give the block and page of
+// this lane's slot i.
+template <int NPT, class Idx, class Page, class Out>
+__device__ __forceinline__ void emit(const uint32_t (&key)[NPT], Idx&& idx_of, Page&& page_of,
+                                     uint32_t T, int kk, int lane, Out&& out) {
     int n_gt = 0;
-    uint64_t gt[NPT], eq[NPT];
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        gt[i] = __ballot(key[i] > T);
-        eq[i] = __ballot(key[i] == T);
-        n_gt += __popcll(gt[i]);
-    }
+    for (int i = 0; i < NPT; ++i) n_gt += __popcll(__ballot(key[i] > T));
     const int need = kk - n_gt;  // keys equal to T still to take, lowest blocks first
     int eq_before = 0, sel_before = 0;
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const bool is_eq = (eq[i] >> lane) & 1ull;
-        const bool take = ((gt[i] >> lane) & 1ull) || (is_eq && eq_before + mbcnt(eq[i]) < need);
+    for (int i = 0; i < NPT; ++i) {  // masks are formed where used: no per-slot arrays
+        const uint64_t eq = __ballot(key[i] == T);
+        const bool take = key[i] > T || (key[i] == T && eq_before + mbcnt(eq) < need);
         const uint64_t sm = __ballot(take);
-        if (take) {
-            const int pos = sel_before + mbcnt(sm);
-            out[pos] = idx[i];
-            if (out_score) out_score[pos] = raw[i];
-        }
-        eq_before += __popcll(eq[i]);
+        if (take) out(sel_before + mbcnt(sm), key[i], idx_of(i), page_of(i));
+        eq_before += __popcll(eq);
         sel_before += __popcll(sm);
     }
-    if (lane >= kk && lane < kTopK) {
-        out[lane] = -1;
-        if (out_score) out_score[lane] = 0.f;
-    }
+    if (lane >= kk && lane < kTopK) out(lane, 0u, -1, -1);
 }
 
-// Scratch of the W-wavefront selection: each wavefront's local winners.
+// Wave-level selection over keys at positions slot*64 + lane (key 0 = empty)
+// of which n are candidates; surv is this wavefront's own 64-entry LDS
+// scratch.  Every lane of the wavefront calls it.
+template <int NPT, class Idx, class Page, class Out>
+__device__ void select_wave(const uint32_t (&key)[NPT], Idx&& idx_of, Page&& page_of, int n,
+                            int lane, Cand* surv, Out&& out) {
+    const int kk = n < kTopK ? n : kTopK;
+    if (n <= kTopK) {  // every candidate is kept
+        emit<NPT>(key, idx_of, page_of, 1u, kk, lane, out);
+        return;
+    }
+    if constexpr (NPT > 1) {
+        // 1. threshold from the lane maxima (n > k candidates fill > k lanes)
+        uint32_t lm[1] = {key[0]};
+#pragma unroll
+        for (int i = 1; i < NPT; ++i) lm[0] = max(lm[0], key[i]);
+        const uint32_t T0 = kth_key<1>(lm, kk);
+        // 2. compact the keys >= T0 in (slot, lane) order
+        int tot = 0;
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) tot += __popcll(__ballot(key[i] >= T0));
+        if (tot <= kWave) {
+            int before = 0;
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) {
+                const uint64_t sm = __ballot(key[i] >= T0);
+                if (key[i] >= T0) {
+                    Cand c;
+                    c.key = key[i];
+                    c.idx = idx_of(i);
+                    c.page = page_of(i);
+                    c.pad = 0;
+                    surv[before + mbcnt(sm)] = c;
+                }
+                before += __popcll(sm);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            Cand c;
+            c.key = 0u;
+            c.idx = -1;
+            c.page = -1;
+            if (lane < tot) c = surv[lane];
+            const uint32_t k1[1] = {c.key};
+            // 3. exact threshold among the survivors
+            emit<1>(k1, [&](int) { return c.idx; }, [&](int) { return c.page; }, kth_key<1>(k1, kk),
+                    kk, lane, out);
+            return;
+        }
+    }
+    emit<NPT>(key, idx_of, page_of, kth_key<NPT>(key, kk), kk, lane, out);
+}
+
+// LDS of a W-wavefront row selection: per-wavefront compaction scratch and
+// each wavefront's local winners.
 template <int W>
-struct SelectScratch {
-    int32_t idx[W][kTopK];
-    float score[W][kTopK];
+struct SelectShared {
+    Cand surv[W][kWave];
+    Cand win[W > 1 ? W : 1][kTopK];
 };
 
-// Loads this thread's candidate scores.  W == 1: block i*64 + lane.  W > 1:
-// wavefront w owns the contiguous range [w*NPT*64, (w+1)*NPT*64), block
-// w*NPT*64 + i*64 + lane.  Slots past maxblk read nothing.
-template <int NPT, int W>
-__device__ __forceinline__ void load_candidates(const float* __restrict__ sc, int maxblk, int w,
-                                                int lane, float (&raw)[NPT]) {
+// Candidates of wavefront w: W == 1 owns blocks slot*64 + lane; W > 1 owns the
+// contiguous range [w*NPT*64, (w+1)*NPT*64).  Slots at or past maxblk read
+// nothing.  With PAGES the block-table entry of each candidate is loaded
+// beside its score (bt_row = the sequence's block-table row).
+template <int NPT, int W, bool PAGES>
+__device__ __forceinline__ void load_candidates(const float* __restrict__ sc,
+                                                const int32_t* __restrict__ bt_row, int maxblk,
+                                                int w, int lane, float (&raw)[NPT],
+                                                int (&page)[NPT]) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
         const int c = w * NPT * kWave + i * kWave + lane;
         raw[i] = (c < maxblk) ? sc[c] : 0.f;
+        page[i] = (PAGES && c < maxblk) ? bt_row[c] : -1;
     }
 }
 
-// Selects the row's blocks (eligible: 0..b_loc) and writes kTopK entries to
-// out (global or LDS).  W == 1 is wave-local.  With W > 1 every thread of the
-// W-wavefront workgroup must call it: each wavefront selects its own range's
-// top-k with no barrier, and wavefront 0 selects the final k among the
-// W*k survivors -- which already sit in ascending block order, so the same
-// rule (and tie-break) applies.  The global top-k is contained in the union
-// of the ranges' top-k under that total order.
-template <int NPT, int W>
-__device__ void select_row(const float (&raw)[NPT], int b_loc, int w, int lane,
-                           SelectScratch<W>* sh, int32_t* out) {
-    int idx[NPT];
+// Number of candidates (blocks 0..b_loc) in wavefront w's range.
+template <int NPT>
+__device__ __forceinline__ int wave_candidates(int b_loc, int w) {
+    const int n = b_loc + 1 - w * NPT * kWave;
+    return n < 0 ? 0 : (n > NPT * kWave ? NPT * kWave : n);
+}
+
+// Selects the row's blocks (eligible: 0..b_loc) from the scores loaded by
+// load_candidates and reports them through out(pos, key, block, page).  With
+// W > 1 every thread of the W-wavefront workgroup must call it (one barrier
+// inside) and out is called by wavefront 0 only.
+template <int NPT, int W, class Out>
+__device__ void select_row(const float (&raw)[NPT], const int (&page)[NPT], int b_loc, int w,
+                           int lane, SelectShared<W>* sh, Out&& out) {
+    const int base = w * NPT * kWave;
+    uint32_t key[NPT];
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-        const int c = w * NPT * kWave + i * kWave + lane;
-        idx[i] = c <= b_loc ? c : -1;
+        const int c = base + i * kWave + lane;
+        key[i] = c > b_loc ? 0u : (c == b_loc ? 0xFFFFFFFFu : order_key(raw[i]));
     }
+    const int n = wave_candidates<NPT>(b_loc, w);
+    auto idx_of = [&](int i) { return base + i * kWave + lane; };
+    auto page_of = [&](int i) { return page[i]; };
     if constexpr (W == 1) {
-        select_wave<NPT>(idx, raw, b_loc, lane, out, nullptr);
+        select_wave<NPT>(key, idx_of, page_of, n, lane, sh->surv[0], out);
     } else {
-        select_wave<NPT>(idx, raw, b_loc, lane, sh->idx[w], sh->score[w]);
+        select_wave<NPT>(key, idx_of, page_of, n, lane, sh->surv[w],
+                         [&](int pos, uint32_t k, int b, int pg) {
+                             Cand c;
+                             c.key = k;
+                             c.idx = b;
+                             c.page = pg;
+                             c.pad = 0;
+                             sh->win[w][pos] = c;
+                         });
         __syncthreads();
         if (w == 0) {
             constexpr int N2 = (W * kTopK + kWave - 1) / kWave;
-            int idx2[N2];
-            float raw2[N2];
+            uint32_t key2[N2];
+            int idx2[N2], page2[N2];
 #pragma unroll
             for (int i = 0; i < N2; ++i) {
                 const int pos = i * kWave + lane;
-                const bool ok = pos < W * kTopK;
-                idx2[i] = ok ? sh->idx[pos / kTopK][pos % kTopK] : -1;
-                raw2[i] = ok ? sh->score[pos / kTopK][pos % kTopK] : 0.f;
+                Cand c;
+                c.key = 0u;
+                c.idx = -1;
+                c.page = -1;
+                if (pos < W * kTopK) c = sh->win[pos / kTopK][pos % kTopK];
+                key2[i] = c.key;
+                idx2[i] = c.idx;
+                page2[i] = c.page;
             }
-            select_wave<N2>(idx2, raw2, b_loc, lane, out, nullptr);
+            int n2 = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const int nv = wave_candidates<NPT>(b_loc, v);
+                n2 += nv < kTopK ? nv : kTopK;
+            }
+            select_wave<N2>(key2, [&](int i) { return idx2[i]; }, [&](int i) { return page2[i]; },
+                            n2, lane, sh->surv[0], out);
         }
     }
 }

@@ -6,8 +6,8 @@
 // score, equal scores to the lower block index.  Output: the kept blocks in
 // ascending order, then -1.
 //
-// The selection itself (ordered keys, ballot-counted bitwise threshold
-// search, lower-index tie fill) lives in select.hpp.
+// The selection itself (ordered keys, lane-maximum prefilter, ballot-counted
+// bitwise threshold search, lower-index tie fill) lives in select.hpp.
 //
 // Page table (aivizor news item, paragraph on MSA with paged attention): the
 // KV-group dimension is flattened into the batch and each row's pages are the
@@ -28,17 +28,25 @@ void topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ s
     const int lane = threadIdx.x % kWave;
     const int w = (W == 1) ? 0 : wave;  // wave index within the row
     const int row = (W == 1) ? blockIdx.x * 4 + wave : blockIdx.x;
-    __shared__ SelectScratch<W> sh;
+    // W == 1: one selection scratch per wavefront (each has its own row)
+    __shared__ SelectShared<W> sh[W == 1 ? 4 : 1];
     if (row >= total_rows) return;  // W == 1 only: whole wavefront leaves together
 
     const int t = row / Hkv;
     // score loads do not wait for the sequence lookup; slots past the own
     // block are discarded
     float raw[NPT];
-    load_candidates<NPT, W>(scores + (size_t)row * maxblk, maxblk, w, lane, raw);
-    const SeqInfo si = lookup_seq(cu_q, seq_lens, B, t);
-    const int p = si.L - si.nq + (t - si.q0);
-    select_row<NPT, W>(raw, p / kBlock, w, lane, &sh, sel + (size_t)row * kTopK);
+    int page[NPT];
+    load_candidates<NPT, W, false>(scores + (size_t)row * maxblk, nullptr, maxblk, w, lane, raw,
+                                   page);
+    // cu_q == nullptr: decode, query token t is sequence t's only query
+    const int p = cu_q ? [&] {
+        const SeqInfo si = lookup_seq(cu_q, seq_lens, B, t);
+        return si.L - si.nq + (t - si.q0);
+    }() : seq_lens[t] - 1;
+    int32_t* out = sel + (size_t)row * kTopK;
+    select_row<NPT, W>(raw, page, p / kBlock, w, lane, &sh[W == 1 ? wave : 0],
+                       [&](int pos, uint32_t, int b, int) { out[pos] = b; });
 }
 
 __global__ void page_table_kernel(const int32_t* __restrict__ sel,

@@ -209,3 +209,57 @@ def test_fused_decode_step_repeats_and_long_rows():
             assert torch.equal(fused.out, ref.out), f"{cfg.name} call {i}"
             assert torch.equal(fused.lse, ref.lse), f"{cfg.name} call {i}"
             assert torch.equal(fused.sel, ref.sel), f"{cfg.name} call {i}"
+
+
+@pytest.mark.parametrize("ctx,n_heads", [(60000, (8, 2)), (190000, (4, 1))],
+                         ids=["one_wave_rows", "four_wave_rows"])
+def test_quantised_scores_tie_at_the_threshold(ctx, n_heads):
+    """Scores on 100 levels: a few blocks share each level, so the k-th
+    largest score is usually tied while only a few dozen blocks reach the
+    lane-maximum prefilter -- ties are resolved inside the compacted survivor
+    set.  Selection equals the oracle's on the GPU's scores, and the fused
+    step equals the four calls."""
+    hq, hkv = n_heads
+    cfg = gen.MsaConfig(f"quantised_{ctx}", [ctx, ctx // 3], [1, 1], hq, hkv,
+                        permute_pages=True, seed=46)
+    print(f"[quantised] {cfg.name} maxblk={cfg.max_blocks}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda")
+    rng = np.random.default_rng(1)
+    # level/8 is exact in bf16 for level < 256; q = 1 makes a score 64 * level / 8
+    levels = rng.integers(0, 100, size=(cfg.num_pages, cfg.num_idx_heads)).astype(np.float32)
+    vals = torch.from_numpy(levels / 8.0).cuda()
+    x.kidx_cache.copy_(vals[:, :, None, None].expand_as(x.kidx_cache).to(torch.bfloat16))
+    x.q_idx.fill_(1.0)
+    ref = MsaStep(x)
+    ref.run()
+    torch.cuda.synchronize()
+    sel = parity.check_selection(cfg, x, ref)
+    assert (sel >= 0).sum() == cfg.total_q * cfg.num_kv_heads * cfg.topk
+    fused = MsaStep(x, fused=True)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.sel, ref.sel)
+    assert torch.equal(fused.out, ref.out)
+    assert torch.equal(fused.lse, ref.lse)
+
+
+def test_fused_decode_step_rows_past_8192_blocks():
+    """Rows of more than 8192 blocks select in the standalone kernel inside
+    msa_decode_step; the result still equals the four calls."""
+    cfg = gen.MsaConfig("step_8300_blocks", [8300 * 128 - 5, 3000], [1, 1], 2, 1,
+                        permute_pages=True, seed=47)
+    print(f"[fused-past-8192] maxblk={cfg.max_blocks}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    ref = MsaStep(x)
+    ref.run()
+    for with_sel in (True, False):
+        fused = MsaStep(x, fused=True)
+        fused.sel.fill_(-7)
+        L.msa_decode_step(fused.dims, x.q_idx, x.kidx_cache, x.q, x.k_cache, x.v_cache,
+                          x.block_table, x.seq_lens, fused.out, fused.lse,
+                          fused.sel if with_sel else None, fused.workspace)
+        torch.cuda.synchronize()
+        if with_sel:
+            assert torch.equal(fused.sel, ref.sel)
+        assert torch.equal(fused.out, ref.out)
+        assert torch.equal(fused.lse, ref.lse)
