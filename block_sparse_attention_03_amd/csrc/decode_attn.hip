@@ -277,25 +277,27 @@ void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __res
     const int r = rn / G;
     const int n = rn % G;
     const int d = threadIdx.x;
-    const int npages = min(kTopK, ceil_div(row_lens[r], kBlock));
     DecodeWs w = decode_ws(const_cast<void*>(ws), R, G);
     const float* lp = w.lse + (size_t)r * kTopK * G + n;
-    // all partials' loads are issued before any is used
+    // every slot's partial is loaded together with the row length (slots past
+    // the row's pages hold stale workspace values and are dropped by selects,
+    // never by a multiply, so a stale non-finite value cannot leak in)
     float li[kTopK], oi[kTopK];
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        li[i] = (i < npages) ? lp[i * G] : -__builtin_inff();
-        oi[i] = (i < npages) ? w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d] : 0.f;
+        li[i] = lp[i * G];
+        oi[i] = w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d];
     }
+    const int npages = min(kTopK, ceil_div(row_lens[r], kBlock));
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < kTopK; ++i) mx = fmaxf(mx, li[i]);
+    for (int i = 0; i < kTopK; ++i) mx = (i < npages) ? fmaxf(mx, li[i]) : mx;
     float den = 0.f, acc = 0.f;
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        const float wi = (i < npages) ? __expf(li[i] - mx) : 0.f;
-        den += wi;
-        acc += wi * oi[i];
+        const float wi = __expf(li[i] - mx);
+        den = (i < npages) ? den + wi : den;
+        acc = (i < npages) ? acc + wi * oi[i] : acc;
     }
     const int s = r / Hkv;
     const int h = (r % Hkv) * G + n;

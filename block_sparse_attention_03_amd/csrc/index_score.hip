@@ -48,6 +48,9 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     const int ih = blockIdx.y % Hidx;
     if (b >= maxblk) return;
 
+    // the block-table entry (in bounds for any b < maxblk) is read beside the
+    // sequence length rather than after it
+    const int page = block_table[(size_t)s * maxblk + b];
     const int L = seq_lens[s];
     // cu_q == nullptr: decode, query token s is sequence s's only query
     const int q0 = cu_q ? cu_q[s] : s;
@@ -78,7 +81,6 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
 
     // A operands: the block's index keys.  Tile mt covers tokens 16*mt..16*mt+15;
     // k-step i of lane group kg takes dims 32*i + 8*kg .. +7 of the token row.
-    const int page = block_table[(size_t)s * maxblk + b];
     const uint16_t* kb = kidx + ((size_t)page * Hidx + ih) * kBlock * kIdxDim;
     bf16x8 a[8][2];
 #pragma unroll

@@ -22,11 +22,14 @@
 //      hold a key >= T0), so every key of the selection is >= T0;
 //   2. the keys >= T0 (usually a few more than kk) are compacted, in
 //      ascending block order, one per lane through LDS;
-//   3. the search runs again on that single register.
-// When more than 64 keys are >= T0 (heavy ties) the search runs on all keys.
-// Each search stops early once exactly kk keys are >= the candidate
-// threshold: those keys are then the selection.  Keys above the threshold are
-// kept; among keys equal to it the lowest blocks fill the rest.
+//   3. each survivor counts the survivors ahead of it (larger key, or equal
+//      key and lower block) from broadcast LDS reads of 64-bit (key, order)
+//      values -- vector work only -- and the kk survivors with fewer than kk
+//      ahead are kept.
+// When more than 64 keys are >= T0 (heavy ties) the search runs on all keys;
+// keys above its threshold are kept and among keys equal to it the lowest
+// blocks fill the rest.  A search stops early once exactly kk keys are >= the
+// candidate threshold: those keys are then the selection.
 //
 // Long rows are split over W wavefronts, each selecting its range's top-k;
 // wavefront 0 then selects from the W*k survivors, which already sit in
@@ -38,9 +41,10 @@
 namespace msa {
 
 __device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (f == 0.0f) u = 0u;  // -0.0 and +0.0 compare equal
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    // f + 0 turns -0.0 into +0.0 (they compare equal); negative values have
+    // all bits flipped, the others only the sign bit
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 
 struct SeqInfo {
@@ -122,72 +126,108 @@ __device__ __forceinline__ void emit(const uint32_t (&key)[NPT], Idx&& idx_of, P
     if (lane >= kk && lane < kTopK) out(lane, 0u, -1, -1);
 }
 
+// One wavefront's LDS scratch: compacted survivors and their rank keys.
+struct alignas(16) WaveScratch {
+    Cand surv[kWave];
+    uint64_t rkey[kWave];
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One candidate per lane (key 0 = empty), lanes in ascending block order, no
+// candidate at or past lane `span`: a lane's rank is the number of lanes ahead
+// of it (larger key, or equal key and lower lane), and the kk lanes of rank
+// < kk are kept.  Needs kk <= #candidates.
+template <class Out>
+__device__ __forceinline__ void select_ranked(uint32_t key, int idx, int page, int span, int kk,
+                                              int lane, uint64_t* rkey, Out&& out) {
+    // rank key (key, 63 - lane): distinct, and larger means ahead
+    const uint64_t ci = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(kWave - 1 - lane);
+    rkey[lane] = ci;
+    wave_sync_lds();
+    int rank = 0;
+    for (int j0 = 0; j0 < span; j0 += 16) {  // 16 rank keys per pass, read first
+        u64x2 cj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cj[u] = *reinterpret_cast<const u64x2*>(rkey + j0 + 2 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (cj[u][0] > ci ? 1 : 0) + (cj[u][1] > ci ? 1 : 0);
+    }
+    const bool take = key != 0u && rank < kk;
+    const uint64_t sm = __ballot(take);
+    if (take) out(mbcnt(sm), key, idx, page);
+    if (lane >= kk && lane < kTopK) out(lane, 0u, -1, -1);
+}
+
 // Wave-level selection over keys at positions slot*64 + lane (key 0 = empty)
-// of which n are candidates; surv is this wavefront's own 64-entry LDS
-// scratch.  Every lane of the wavefront calls it.
+// of which n are candidates; ws is this wavefront's own LDS scratch.  Every
+// lane of the wavefront calls it.
 template <int NPT, class Idx, class Page, class Out>
 __device__ void select_wave(const uint32_t (&key)[NPT], Idx&& idx_of, Page&& page_of, int n,
-                            int lane, Cand* surv, Out&& out) {
+                            int lane, WaveScratch* ws, Out&& out) {
     const int kk = n < kTopK ? n : kTopK;
     if (n <= kTopK) {  // every candidate is kept
         emit<NPT>(key, idx_of, page_of, 1u, kk, lane, out);
         return;
     }
-    if constexpr (NPT > 1) {
+    if constexpr (NPT == 1) {
+        select_ranked(key[0], idx_of(0), page_of(0), kWave, kk, lane, ws->rkey, out);
+    } else {
         // 1. threshold from the lane maxima (n > k candidates fill > k lanes)
         uint32_t lm[1] = {key[0]};
 #pragma unroll
         for (int i = 1; i < NPT; ++i) lm[0] = max(lm[0], key[i]);
         const uint32_t T0 = kth_key<1>(lm, kk);
-        // 2. compact the keys >= T0 in (slot, lane) order
+        // 2. compact the keys >= T0 in (slot, lane) order; past 64 of them the
+        // scratch is not used
         int tot = 0;
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) tot += __popcll(__ballot(key[i] >= T0));
-        if (tot <= kWave) {
-            int before = 0;
-#pragma unroll
-            for (int i = 0; i < NPT; ++i) {
-                const uint64_t sm = __ballot(key[i] >= T0);
-                if (key[i] >= T0) {
-                    Cand c;
-                    c.key = key[i];
-                    c.idx = idx_of(i);
-                    c.page = page_of(i);
-                    c.pad = 0;
-                    surv[before + mbcnt(sm)] = c;
-                }
-                before += __popcll(sm);
+        for (int i = 0; i < NPT; ++i) {
+            const uint64_t sm = __ballot(key[i] >= T0);
+            const int pos = tot + mbcnt(sm);
+            if (key[i] >= T0 && pos < kWave) {
+                Cand c;
+                c.key = key[i];
+                c.idx = idx_of(i);
+                c.page = page_of(i);
+                c.pad = 0;
+                ws->surv[pos] = c;
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            tot += __popcll(sm);
+        }
+        if (tot <= kWave) {
+            wave_sync_lds();
             Cand c;
             c.key = 0u;
             c.idx = -1;
             c.page = -1;
-            if (lane < tot) c = surv[lane];
-            const uint32_t k1[1] = {c.key};
-            // 3. exact threshold among the survivors
-            emit<1>(k1, [&](int) { return c.idx; }, [&](int) { return c.page; }, kth_key<1>(k1, kk),
-                    kk, lane, out);
+            if (lane < tot) c = ws->surv[lane];
+            // 3. rank the survivors
+            select_ranked(c.key, c.idx, c.page, tot, kk, lane, ws->rkey, out);
             return;
         }
+        emit<NPT>(key, idx_of, page_of, kth_key<NPT>(key, kk), kk, lane, out);
     }
-    emit<NPT>(key, idx_of, page_of, kth_key<NPT>(key, kk), kk, lane, out);
 }
 
 // LDS of a W-wavefront row selection: per-wavefront compaction scratch and
 // each wavefront's local winners.
 template <int W>
 struct SelectShared {
-    Cand surv[W][kWave];
+    WaveScratch ws[W];
     Cand win[W > 1 ? W : 1][kTopK];
 };
 
 // Candidates of wavefront w: W == 1 owns blocks slot*64 + lane; W > 1 owns the
-// contiguous range [w*NPT*64, (w+1)*NPT*64).  Slots at or past maxblk read
-// nothing.  With PAGES the block-table entry of each candidate is loaded
-// beside its score (bt_row = the sequence's block-table row).
+// contiguous range [w*NPT*64, (w+1)*NPT*64).  Slots at or past maxblk re-read
+// the last block (they are past b_loc, so their values are never used): the
+// loads carry no condition and are all in flight together.  With PAGES the
+// block-table entry of each candidate is loaded beside its score (bt_row = the
+// sequence's block-table row).
 template <int NPT, int W, bool PAGES>
 __device__ __forceinline__ void load_candidates(const float* __restrict__ sc,
                                                 const int32_t* __restrict__ bt_row, int maxblk,
@@ -195,9 +235,9 @@ __device__ __forceinline__ void load_candidates(const float* __restrict__ sc,
                                                 int (&page)[NPT]) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-        const int c = w * NPT * kWave + i * kWave + lane;
-        raw[i] = (c < maxblk) ? sc[c] : 0.f;
-        page[i] = (PAGES && c < maxblk) ? bt_row[c] : -1;
+        const int c = min(w * NPT * kWave + i * kWave + lane, maxblk - 1);
+        raw[i] = sc[c];
+        page[i] = PAGES ? bt_row[c] : -1;
     }
 }
 
@@ -226,9 +266,9 @@ __device__ void select_row(const float (&raw)[NPT], const int (&page)[NPT], int 
     auto idx_of = [&](int i) { return base + i * kWave + lane; };
     auto page_of = [&](int i) { return page[i]; };
     if constexpr (W == 1) {
-        select_wave<NPT>(key, idx_of, page_of, n, lane, sh->surv[0], out);
+        select_wave<NPT>(key, idx_of, page_of, n, lane, &sh->ws[0], out);
     } else {
-        select_wave<NPT>(key, idx_of, page_of, n, lane, sh->surv[w],
+        select_wave<NPT>(key, idx_of, page_of, n, lane, &sh->ws[w],
                          [&](int pos, uint32_t k, int b, int pg) {
                              Cand c;
                              c.key = k;
@@ -261,7 +301,7 @@ __device__ void select_row(const float (&raw)[NPT], const int (&page)[NPT], int 
                 n2 += nv < kTopK ? nv : kTopK;
             }
             select_wave<N2>(key2, [&](int i) { return idx2[i]; }, [&](int i) { return page2[i]; },
-                            n2, lane, sh->surv[0], out);
+                            n2, lane, &sh->ws[0], out);
         }
     }
 }
