@@ -35,66 +35,131 @@ constexpr int kVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B: the tr
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Inverse-map tiles: the selections of one KV group over kTileTokens
+// consecutive query tokens of one sequence.
+constexpr int kTileTokens = 512;
+constexpr int kMapThreads = 256;
+
+// Upper bound on the number of tiles (sum over sequences of ceil(nq / tile)
+// is at most total_q / tile + B), times the KV groups.
+__host__ __device__ inline int max_tiles(int total_q, int B, int Hkv) {
+    return Hkv * (ceil_div(total_q, kTileTokens) + B);
+}
+
 struct PrefillWs {
-    int32_t* counts;   // [NB]
-    int32_t* offsets;  // [NB + 1]
-    int32_t* cursor;   // [NB]
-    int32_t* entries;  // [total_q * Hkv * k]: query << 4 | slot
-    uint16_t* part_o;  // [total_q, Hq, k, 128] bf16
-    float* part_lse;   // [total_q, Hq, k]
+    int32_t* counts;     // [NB] entries per (sequence, group, block) bucket
+    int32_t* offsets;    // [NB + 1] exclusive scan of counts
+    int32_t* tile_base;  // [max_tiles, maxblk] a tile's first position within a bucket
+    int32_t* entries;    // [total_q * Hkv * k]: query << 4 | slot, grouped by bucket
+    uint16_t* part_o;    // [total_q, Hq, k, 128] bf16
+    float* part_lse;     // [total_q, Hq, k]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-__host__ __device__ inline PrefillWs prefill_ws(void* base, int NB, int total_q, int Hq, int Hkv) {
+__host__ __device__ inline PrefillWs prefill_ws(void* base, int B, int Hkv, int maxblk,
+                                                int total_q, int Hq) {
+    const size_t NB = (size_t)B * Hkv * maxblk;
     char* p = static_cast<char*>(base);
     PrefillWs w;
     w.counts = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)NB * 4);
+    p += align256(NB * 4);
     w.offsets = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)(NB + 1) * 4);
-    w.cursor = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)NB * 4);
+    p += align256((NB + 1) * 4);
+    w.tile_base = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)max_tiles(total_q, B, Hkv) * maxblk * 4);
     w.entries = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)total_q * Hkv * kTopK * 4);
     w.part_o = reinterpret_cast<uint16_t*>(p);
     p += align256((size_t)total_q * Hq * kTopK * kHeadDim * 2);
     w.part_lse = reinterpret_cast<float*>(p);
-    p += align256((size_t)total_q * Hq * kTopK * 4);
     return w;
 }
 
-__host__ __device__ inline size_t prefill_ws_size(int NB, int total_q, int Hq, int Hkv) {
-    PrefillWs w = prefill_ws(nullptr, NB, total_q, Hq, Hkv);
+__host__ __device__ inline size_t prefill_ws_size(int B, int Hkv, int maxblk, int total_q, int Hq) {
+    PrefillWs w = prefill_ws(nullptr, B, Hkv, maxblk, total_q, Hq);
     return reinterpret_cast<size_t>(w.part_lse) + align256((size_t)total_q * Hq * kTopK * 4);
 }
 
-__device__ __forceinline__ int seq_of_token(const int32_t* cu_q, int B, int t) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+__global__ void zero_kernel(int32_t* a, int na) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na; i += gridDim.x * blockDim.x) a[i] = 0;
 }
 
-__global__ void zero_kernel(int32_t* a, int na, int32_t* b, int nb) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < na || i < nb; i += gridDim.x * blockDim.x) {
-        if (i < na) a[i] = 0;
-        if (i < nb) b[i] = 0;
+struct MapTile {
+    int s, g, t0, t1;  // sequence, KV group, query tokens [t0, t1); s < 0: no such tile
+};
+
+// Tile `tile` = (group tile % Hkv, k-th (sequence, token chunk) pair in
+// sequence order, k = tile / Hkv).  Wavefront 0 finds the pair -- lanes count
+// the chunks of 64 sequences at a time and a prefix over lanes locates k -- and
+// publishes it through sh; every thread must call it (one barrier).
+__device__ MapTile find_map_tile(const int32_t* __restrict__ cu_q, int B, int Hkv, int tile,
+                                 int* sh) {
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        int k = tile / Hkv;
+        int found = -1, chunk = 0;
+        for (int base = 0; base < B && found < 0; base += kWave) {
+            const int i = base + lane;
+            const int nq = i < B ? cu_q[i + 1] - cu_q[i] : 0;
+            const int n = ceil_div(nq, kTileTokens);
+            int incl = n;  // inclusive prefix of chunk counts over lanes
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int v = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += v;
+            }
+            const uint64_t hit = __ballot(incl > k);
+            if (hit) {
+                const int l = __ffsll((unsigned long long)hit) - 1;
+                found = base + l;
+                chunk = k - (__shfl(incl, l, kWave) - __shfl(n, l, kWave));
+            } else {
+                k -= __shfl(incl, kWave - 1, kWave);
+            }
+        }
+        if (lane == 0) {
+            sh[0] = found;
+            sh[1] = chunk;
+        }
     }
+    __syncthreads();
+    MapTile m;
+    m.s = sh[0];
+    m.g = tile % Hkv;
+    m.t0 = m.t1 = 0;
+    if (m.s >= 0) {
+        m.t0 = cu_q[m.s] + sh[1] * kTileTokens;
+        m.t1 = min(cu_q[m.s + 1], m.t0 + kTileTokens);
+    }
+    return m;
 }
 
-__global__ void histogram_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
-                                 int32_t* __restrict__ counts, int B, int Hkv, int maxblk, int n) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n) return;
-    const int b = sel[idx];
-    if (b < 0) return;
-    const int t = idx / (Hkv * kTopK);
-    const int g = (idx / kTopK) % Hkv;
-    const int s = seq_of_token(cu_q, B, t);
-    atomicAdd(&counts[((size_t)s * Hkv + g) * maxblk + b], 1);
+// Pass 1: a tile counts its selections per block in LDS, then adds each
+// nonzero count to the bucket's global count with one atomic; the value that
+// atomic returns is the tile's first position within the bucket.  Block
+// indices outside [0, maxblk) are not selections.
+__global__ __launch_bounds__(kMapThreads)
+void bucket_count_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
+                         int32_t* __restrict__ counts, int32_t* __restrict__ tile_base, int B,
+                         int Hkv, int maxblk) {
+    extern __shared__ int32_t hist[];  // [maxblk]
+    __shared__ int sh[2];
+    for (int b = threadIdx.x; b < maxblk; b += kMapThreads) hist[b] = 0;
+    const MapTile m = find_map_tile(cu_q, B, Hkv, blockIdx.x, sh);  // contains a barrier
+    if (m.s < 0) return;  // uniform
+    const int n = (m.t1 - m.t0) * kTopK;
+    for (int e = threadIdx.x; e < n; e += kMapThreads) {
+        const int t = m.t0 + e / kTopK;
+        const int b = sel[((size_t)t * Hkv + m.g) * kTopK + e % kTopK];
+        if (b >= 0 && b < maxblk) atomicAdd(&hist[b], 1);
+    }
+    __syncthreads();
+    const size_t bucket0 = ((size_t)m.s * Hkv + m.g) * maxblk;
+    for (int b = threadIdx.x; b < maxblk; b += kMapThreads) {
+        const int c = hist[b];
+        if (c > 0) tile_base[(size_t)blockIdx.x * maxblk + b] = atomicAdd(&counts[bucket0 + b], c);
+    }
 }
 
 // Exclusive scan of counts[0..n) into offsets[0..n], one workgroup.
@@ -122,20 +187,30 @@ void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offse
     if (tid == 1023) offsets[n] = part[1023];
 }
 
-__global__ void scatter_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
-                               const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                               int32_t* __restrict__ entries, int B, int Hkv, int maxblk, int n) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n) return;
-    const int b = sel[idx];
-    if (b < 0) return;
-    const int t = idx / (Hkv * kTopK);
-    const int g = (idx / kTopK) % Hkv;
-    const int slot = idx % kTopK;
-    const int s = seq_of_token(cu_q, B, t);
-    const size_t bk = ((size_t)s * Hkv + g) * maxblk + b;
-    const int pos = offsets[bk] + atomicAdd(&cursor[bk], 1);
-    entries[pos] = (t << 4) | slot;
+// Pass 3: the tile places each selection at offsets[bucket] + its tile's base
+// in the bucket + its rank among the tile's selections of that block (LDS
+// counters; entries within a bucket are in no particular order).
+__global__ __launch_bounds__(kMapThreads)
+void bucket_fill_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
+                        const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_base,
+                        int32_t* __restrict__ entries, int B, int Hkv, int maxblk) {
+    extern __shared__ int32_t cur[];  // [maxblk]
+    __shared__ int sh[2];
+    for (int b = threadIdx.x; b < maxblk; b += kMapThreads) cur[b] = 0;
+    const MapTile m = find_map_tile(cu_q, B, Hkv, blockIdx.x, sh);  // contains a barrier
+    if (m.s < 0) return;  // uniform
+    const int n = (m.t1 - m.t0) * kTopK;
+    const size_t bucket0 = ((size_t)m.s * Hkv + m.g) * maxblk;
+    for (int e = threadIdx.x; e < n; e += kMapThreads) {
+        const int t = m.t0 + e / kTopK;
+        const int slot = e % kTopK;
+        const int b = sel[((size_t)t * Hkv + m.g) * kTopK + slot];
+        if (b >= 0 && b < maxblk) {
+            const int pos = offsets[bucket0 + b] + tile_base[(size_t)blockIdx.x * maxblk + b] +
+                            atomicAdd(&cur[b], 1);
+            entries[pos] = (t << 4) | slot;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kPfThreads, 1)
@@ -426,8 +501,7 @@ void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
 
 size_t msa_prefill_ws_bytes(const MsaShape& s, int total_q) {
     using namespace msa;
-    const int NB = s.B * s.Hkv * s.maxblk;
-    return prefill_ws_size(NB, total_q, s.Hq, s.Hkv);
+    return prefill_ws_size(s.B, s.Hkv, s.maxblk, total_q, s.Hq);
 }
 
 hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
@@ -438,15 +512,16 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     using namespace msa;
     if (total_q == 0) return hipSuccess;
     const int NB = s.B * s.Hkv * s.maxblk;
-    PrefillWs w = prefill_ws(ws, NB, total_q, s.Hq, s.Hkv);
-    const int n_sel = total_q * s.Hkv * kTopK;
+    PrefillWs w = prefill_ws(ws, s.B, s.Hkv, s.maxblk, total_q, s.Hq);
+    const int tiles = max_tiles(total_q, s.B, s.Hkv);
+    const size_t map_lds = (size_t)s.maxblk * sizeof(int32_t);
     hipLaunchKernelGGL(zero_kernel, dim3(min(1024, ceil_div(NB, 256))), dim3(256), 0, st,
-                       w.counts, NB, w.cursor, NB);
-    hipLaunchKernelGGL(histogram_kernel, dim3(ceil_div(n_sel, 256)), dim3(256), 0, st, sel, cu_q,
-                       w.counts, s.B, s.Hkv, s.maxblk, n_sel);
+                       w.counts, NB);
+    hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
+                       w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, NB);
-    hipLaunchKernelGGL(scatter_kernel, dim3(ceil_div(n_sel, 256)), dim3(256), 0, st, sel, cu_q,
-                       w.offsets, w.cursor, w.entries, s.B, s.Hkv, s.maxblk, n_sel);
+    hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
+                       w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
     hipLaunchKernelGGL(block_major_kernel, dim3(NB), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
                        block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
