@@ -133,8 +133,10 @@ constexpr int kGWaves = 8;                       // wavefronts per workgroup
 constexpr int kGTiles = 4;                       // 32-row tiles per wavefront
 constexpr int kGRows = kGWaves * kGTiles * 32;   // rows per workgroup (1024)
 constexpr int kGBlocks = 64;                     // blocks per workgroup chunk
-constexpr int kGSub = 8;                         // blocks whose maxima are held at once
 constexpr int kKStrideB = kIdxDim * 2 + 16;      // bytes per LDS index-key row (padded)
+// s_waitcnt immediate: vector-memory count 0, the other counters unconstrained
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Which (sequence, row group) this workgroup serves.  Sequence s has
 // ceil(nq_s * R / kGRows) row groups; group ids are dealt out in sequence order.
@@ -174,7 +176,7 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
                              const int32_t* __restrict__ cu_q,
                              float* __restrict__ scores,           // [T, Hkv, maxblk]
                              int B, int Hkv, int Hidx, int maxblk) {
-    __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kBlock * kKStrideB];
+    __shared__ __attribute__((aligned(16))) unsigned char ktile[4][kBlock * kKStrideB];
     __shared__ int grp[2];
 
     const int tid = threadIdx.x;
@@ -246,73 +248,79 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
         }
     };
 
-    u32x4 stage[2];
-    if (b_begin < b_vis_end) {
-        load_tile(b_begin, stage);
-        store_tile(0, stage);
-    }
+    // Blocks go in pairs (b_begin is even) through four LDS tile buffers: the
+    // pair (b0, b0 + 1) sits in buffers cur, cur + 1 while the next pair is
+    // fetched into registers; at the end of the pair those registers go to the
+    // other two buffers and one barrier publishes them.  Each fetch has two
+    // blocks of work to arrive, and every load is waited for inside the
+    // iteration that issued it.
+    u32x4 stage0[2], stage1[2];
+    if (b_begin < b_vis_end) load_tile(b_begin, stage0);
+    if (b_begin + 1 < b_vis_end) load_tile(b_begin + 1, stage1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // every path: nothing outstanding
+    if (b_begin < b_vis_end) store_tile(0, stage0);
+    if (b_begin + 1 < b_vis_end) store_tile(1, stage1);
     __syncthreads();
 
-    for (int sub = b_begin; sub < b_end; sub += kGSub) {
-        float mx[kGTiles][kGSub];
+    // Block b from LDS buffer buf: per-row maxima over this lane half's tokens.
+    auto do_block = [&](int b, int buf, float (&mx)[kGTiles]) {
 #pragma unroll
-        for (int bb = 0; bb < kGSub; ++bb) {
-            const int b = sub + bb;
+        for (int r = 0; r < kGTiles; ++r) mx[r] = -__builtin_inff();
+        if (b >= b_vis_end) return;  // workgroup-uniform
+        const unsigned char* kt = ktile[buf];
+        const int tok_base = b * kBlock;
+        const bool need_mask = tok_base + kBlock - 1 > p_first;
 #pragma unroll
-            for (int r = 0; r < kGTiles; ++r) mx[r][bb] = -__builtin_inff();
-            if (b >= b_vis_end) continue;  // workgroup-uniform
-            const int buf = (b - b_begin) & 1;
-            const bool more = b + 1 < b_vis_end;
-            if (more) load_tile(b + 1, stage);
-            const unsigned char* kt = ktile[buf];
-            const int tok_base = b * kBlock;
-            const bool need_mask = tok_base + kBlock - 1 > p_first;
+        for (int tt = 0; tt < 4; ++tt) {
+            bf16x8 a[4];
+            const unsigned char* arow = kt + (32 * tt + n) * kKStrideB + 64 * h;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                bf16x8 a[4];
-                const unsigned char* arow = kt + (32 * tt + n) * kKStrideB + 64 * h;
+            for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * i));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * i));
+            for (int r = 0; r < kGTiles; ++r) {
+                f32x16 acc = {};
 #pragma unroll
-                for (int r = 0; r < kGTiles; ++r) {
-                    f32x16 acc = {};
+                for (int i = 0; i < 4; ++i) acc = mfma32(a[i], qb[r][i], acc);
+                float m = -__builtin_inff();
+                if (need_mask) {
+                    // value v is token tok_base + 32tt + 8(v/4) + 4h + v%4 of row n
+                    const int lim = prow[r] - tok_base - 32 * tt - 4 * h;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc = mfma32(a[i], qb[r][i], acc);
-                    float m = -__builtin_inff();
-                    if (need_mask) {
-                        // value v is token tok_base + 32tt + 8(v/4) + 4h + v%4 of row n
-                        const int lim = prow[r] - tok_base - 32 * tt - 4 * h;
+                    for (int v = 0; v < 16; ++v)
+                        m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[v] : -__builtin_inff());
+                } else {
 #pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[v] : -__builtin_inff());
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[v]);
-                    }
-                    mx[r][bb] = fmaxf(mx[r][bb], m);
+                    for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[v]);
                 }
+                mx[r] = fmaxf(mx[r], m);
             }
-            if (more) store_tile(buf ^ 1, stage);
-            __syncthreads();
         }
+    };
+
+    for (int b0 = b_begin, cur = 0; b0 < b_end; b0 += 2, cur ^= 2) {
+        if (b0 + 2 < b_vis_end) load_tile(b0 + 2, stage0);
+        if (b0 + 3 < b_vis_end) load_tile(b0 + 3, stage1);
+        float m0[kGTiles], m1[kGTiles];
+        do_block(b0, cur, m0);
+        do_block(b0 + 1, cur + 1, m1);
         // both lane halves saw different tokens of the same row: combine, then
-        // half h writes blocks 4h .. 4h+3 of the sub-chunk
+        // half h writes block b0 + h
 #pragma unroll
         for (int r = 0; r < kGTiles; ++r) {
-#pragma unroll
-            for (int bb = 0; bb < kGSub; ++bb) mx[r][bb] = fmaxf(mx[r][bb], __shfl_xor(mx[r][bb], 32, kWave));
-            if (!rok[r]) continue;
+            m0[r] = fmaxf(m0[r], __shfl_xor(m0[r], 32, kWave));
+            m1[r] = fmaxf(m1[r], __shfl_xor(m1[r], 32, kWave));
+            const int b = b0 + h;
+            if (!rok[r] || b >= b_end) continue;
             const int rho = row0 + (wave * kGTiles + r) * 32 + n;
             const int t = q0 + rho / R;
             const int g = (Hidx == 1) ? rho % R : ih;
-            float* dst = scores + ((size_t)t * Hkv + g) * maxblk;
-#pragma unroll
-            for (int bb = 0; bb < kGSub / 2; ++bb) {
-                const int b = sub + 4 * h + bb;
-                const float v = h ? mx[r][4 + bb] : mx[r][bb];
-                if (b < b_end) dst[b] = v;
-            }
+            scores[((size_t)t * Hkv + g) * maxblk + b] = h ? m1[r] : m0[r];
         }
+        // buffers cur ^ 2, (cur ^ 2) + 1 were last read in the previous pair,
+        // which every wavefront finished before that pair's barrier
+        if (b0 + 2 < b_vis_end) store_tile(cur ^ 2, stage0);
+        if (b0 + 3 < b_vis_end) store_tile((cur ^ 2) + 1, stage1);
+        __syncthreads();
     }
 }
 

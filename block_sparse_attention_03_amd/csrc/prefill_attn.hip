@@ -451,7 +451,7 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 __global__ __launch_bounds__(256)
 void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
                           uint16_t* __restrict__ out, float* __restrict__ lse_out, int total_q,
-                          int Hq, int Hkv) {
+                          int Hq, int Hkv, int maxblk) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int th = idx / 16;  // t * Hq + h
     const int part = idx % 16;
@@ -461,31 +461,35 @@ void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
     const int g = hh / (Hq / Hkv);
     const int32_t* srow = sel + ((size_t)t * Hkv + g) * kTopK;
     const float* lp = w.part_lse + (size_t)th * kTopK;
-    // every slot's loads are issued before any is used
-    int bsel[kTopK];
+    // every slot's partial is loaded together with the selection (a slot that
+    // is not a selection -- index outside [0, maxblk) -- holds stale workspace
+    // values and is dropped by selects, never by a multiply)
+    bool ok[kTopK];
     float li[kTopK];
     u32x4 oi[kTopK];
 #pragma unroll
-    for (int i = 0; i < kTopK; ++i) bsel[i] = srow[i];
+    for (int i = 0; i < kTopK; ++i) {
+        li[i] = lp[i];
+        oi[i] = ld16_stream(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part);
+    }
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        li[i] = bsel[i] >= 0 ? lp[i] : -__builtin_inff();
-        oi[i] = bsel[i] >= 0 ? ld16_stream(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part)
-                             : u32x4{0u, 0u, 0u, 0u};
+        const int b = srow[i];
+        ok[i] = b >= 0 && b < maxblk;
     }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < kTopK; ++i) mx = fmaxf(mx, li[i]);
+    for (int i = 0; i < kTopK; ++i) mx = ok[i] ? fmaxf(mx, li[i]) : mx;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        const float wi = bsel[i] >= 0 ? __expf(li[i] - mx) : 0.f;
-        den += wi;
+        const float wi = __expf(li[i] - mx);
+        den = ok[i] ? den + wi : den;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += wi * bf16_lo(oi[i][e]);
-            acc[2 * e + 1] += wi * bf16_hi(oi[i][e]);
+            acc[2 * e] = ok[i] ? acc[2 * e] + wi * bf16_lo(oi[i][e]) : acc[2 * e];
+            acc[2 * e + 1] = ok[i] ? acc[2 * e + 1] + wi * bf16_hi(oi[i][e]) : acc[2 * e + 1];
         }
     }
     const float inv = 1.0f / den;
@@ -527,6 +531,6 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                        s.scale * kLog2e);
     const int nth = total_q * s.Hq * 16;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
-                       out, lse, total_q, s.Hq, s.Hkv);
+                       out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
     return hipGetLastError();
 }
