@@ -18,10 +18,14 @@ each other with no host or timing gaps.  One pair of HIP events on the
 kernels' stream brackets the K steps; ``value`` is their mean.  The roofline
 kernel is timed the same way: K back-to-back calls of it over the layers.
 
-Also reported (``also``): 1M-context decode (batch 4), with its scoring pass
-measured separately, and 8192-token chunked prefill onto a 57,344-token
-prefix (tokens/s).  The oracle's CPU time on the headline workload is
-reported as ``cpu_baseline``.
+Also reported (``also``): decode at 4096 tokens (batch 1), ragged decode (16
+sequences, 4096 to 524,288 tokens), 1M-context decode (batch 4) with its
+scoring pass measured separately, and 8192-token chunked prefill onto a
+57,344-token prefix (tokens/s).  The headline layer-step is also timed as one
+HIP graph per pass over the layers.  Roofline fractions are given against the
+published peaks and against ceilings measured in the same run
+(``measured_ceilings``: a streaming read and a matrix-core loop).  The
+oracle's CPU time on the headline workload is reported as ``cpu_baseline``.
 """
 from __future__ import annotations
 
@@ -114,6 +118,27 @@ def time_calls(fns, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def time_graph(steps_, steps, warmup):
+    """Mean ms per layer-step when the layer-steps of all layers are captured as
+    one HIP graph and the graph is replayed back to back."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for st in steps_:
+            st.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for st in steps_:
+            st.run()
+    reps = max(1, steps // len(steps_))
+    ms = time_calls([g.replay], reps, max(1, warmup // len(steps_)))
+    del g
+    return ms / len(steps_)
+
+
 def make_layers(cfg, n, device="cuda"):
     """n independent instances of the workload (layer l draws with seed + 1000*l)."""
     import dataclasses
@@ -176,6 +201,47 @@ def recorded_traffic():
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
+def measured_ceilings():
+    """Sustained HBM read bandwidth (a 2 GiB streaming read) and bf16 matrix-core
+    rate (independent 32x32x16 products, 4 waves per SIMD) on this GPU, from the
+    separate calibration library."""
+    import ctypes
+    import os
+    import torch
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_03_amd",
+                        "libmsa_calib.so")
+    c = ctypes.CDLL(path)
+    c.msa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    c.msa_calib_read_sink_len.restype = ctypes.c_size_t
+    c.msa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    c.msa_calib_mfma_flop.restype = ctypes.c_double
+    c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(c.msa_calib_read_sink_len(), dtype=torch.int32, device="cuda")
+    blocks, iters = 1024, 16384
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def read():
+        if c.msa_calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), st) != 0:
+            raise RuntimeError("msa_calib_read failed")
+
+    def mfma():
+        if c.msa_calib_mfma(out.data_ptr(), blocks, iters, st) != 0:
+            raise RuntimeError("msa_calib_mfma failed")
+
+    read_ms = time_calls([read], 5, 2)
+    mfma_ms = time_calls([mfma], 3, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "mfma_bf16_tflops": round(c.msa_calib_mfma_flop(blocks, iters) / (mfma_ms * 1e-3) / 1e12, 1),
+            "how": "2 GiB non-temporal streaming read; 32x32x16 bf16 MFMA loop, 4 independent "
+                   "chains per wave, 16 waves per CU"}
+
+
 def roofline_entry(name, nbytes, ms, traffic=None):
     from block_sparse_attention_03_amd.accounting import HBM_PEAK_GBS
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -222,6 +288,7 @@ def main():
     four = [MsaStep(x) for x in layers]                # the four ABI calls
     fused_ms = time_calls([s.run for s in fused], args.steps, args.warmup)
     four_ms = time_calls([s.run for s in four], args.steps, args.warmup)
+    graph_ms = time_graph(fused, args.steps, args.warmup)
     # roofline kernel: index_score_kernel, a single-kernel call (it and the
     # page kernel each move about half of the step's bytes)
     score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
@@ -255,6 +322,7 @@ def main():
                                    recorded_traffic()),
         "layer_step": {"algorithmic_bytes": layer_bytes,
                        "hbm_frac": frac(fused_ms),
+                       "us_hip_graph": round(graph_ms * 1e3, 2),
                        "us_four_calls": round(four_ms * 1e3, 2),
                        "hbm_frac_four_calls": frac(four_ms),
                        "decode_attention_call": roofline_entry(
@@ -265,9 +333,37 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds)
     del fused, four, layers
     torch.cuda.empty_cache()
+    ceil = measured_ceilings()
+    result["measured_ceilings"] = ceil
+    result["roofline"]["frac_of_measured"] = round(
+        result["roofline"]["achieved"] / ceil["hbm_read_gbs"], 4)
+    result["layer_step"]["hbm_frac_of_measured"] = round(
+        result["layer_step"]["hbm_frac"] * acc.HBM_PEAK_GBS / ceil["hbm_read_gbs"], 4)
 
     if not args.no_also:
         also = {}
+
+        def decode_line(c, n_layers, n_steps):
+            ls = make_layers(c, n_layers)
+            f = [MsaStep(x, fused=True) for x in ls]
+            fo = [MsaStep(x) for x in ls]
+            ms_ = time_calls([st.run for st in f], n_steps, 4)
+            ms4_ = time_calls([st.run for st in fo], n_steps, 4)
+            b_ = acc.score_bytes(c) + acc.decode_attn_bytes(c)
+            line = {"us_per_layer_step": round(ms_ * 1e3, 2),
+                    "layer_step_hbm_frac": round(b_ / (ms_ * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes": int(b_),
+                    "us_four_calls": round(ms4_ * 1e3, 2), "layers": n_layers}
+            del f, fo, ls
+            torch.cuda.empty_cache()
+            return line
+
+        # decode at 4096 tokens, batch 1 (2.6 MB: launch-bound)
+        c1 = gen.config(1)
+        also[c1.name] = decode_line(c1, 128, max(128, args.steps))
+        # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
+        c5 = gen.config(5)
+        also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4))
         # 1M-context decode, batch 4 (18 GB of K/V per layer): 2 layers
         c4 = gen.config(4)
         l4 = make_layers(c4, 2)
@@ -298,8 +394,10 @@ def main():
             "ms_per_step": round(ms3, 4),
             "sparse_attn_call_ms": round(attn3, 4),
             "sparse_attn_call_mfma_frac": round(tf(fl_attn, attn3) / acc.BF16_PEAK_TFLOPS, 4),
+            "sparse_attn_call_mfma_frac_of_measured": round(tf(fl_attn, attn3) / ceil["mfma_bf16_tflops"], 4),
             "index_score_ms": round(score3, 4),
             "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
+            "index_score_mfma_frac_of_measured": round(tf(fl_score, score3) / ceil["mfma_bf16_tflops"], 4),
             "attn_flops": fl_attn, "score_flops": fl_score}
         del s3, l3
         torch.cuda.empty_cache()

@@ -1,0 +1,94 @@
+// ceilings.hip -- measured ceilings for the roofline fractions: a streaming
+// HBM read and a bf16 matrix-core loop on MI355X (gfx950).  Not part of the
+// MSA library: the benchmark loads this separate libmsa_calib.so to report
+// achieved bandwidth and FLOP rate against what the chip actually sustains,
+// next to the published peaks.
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+
+// Every 16-byte chunk of buf read once with streaming (non-temporal) loads,
+// eight in flight per thread; one word per thread goes to sink so the loads
+// cannot be dropped.
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ buf, size_t n16,
+                                                        uint32_t* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+// Four independent chains of 32x32x16 bf16 products per wavefront, iters
+// rounds: the matrix core's sustained rate with 4 waves per SIMD.
+__global__ __launch_bounds__(kThreads) void mfma_kernel(float* __restrict__ out, int iters) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (threadIdx.x + i));
+        b[i] = (__bf16)(0.002f * (blockIdx.x % 7 - i));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Workgroups of the read kernel; sink must hold msa_calib_read_sink_len() words.
+int msa_calib_read_blocks(void) { return 4096; }
+size_t msa_calib_read_sink_len(void) { return (size_t)4096 * kThreads; }
+
+// Streams `bytes` (a multiple of 16) of device memory at buf.  Returns a
+// hipError_t value (0 = launched).
+int msa_calib_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_len, void* stream) {
+    if (!buf || !sink || bytes % 16 != 0 || sink_len < msa_calib_read_sink_len())
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_kernel, dim3(msa_calib_read_blocks()), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), bytes / 16,
+                       sink);
+    return (int)hipGetLastError();
+}
+
+// bf16 FLOP of one msa_calib_mfma launch of `blocks` workgroups.
+double msa_calib_mfma_flop(int blocks, int iters) {
+    return (double)blocks * (kThreads / 64) * iters * 4 * (32.0 * 32.0 * 16.0 * 2.0);
+}
+
+// out must hold blocks * 256 floats.
+int msa_calib_mfma(float* out, int blocks, int iters, void* stream) {
+    if (!out || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       out, iters);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"
