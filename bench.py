@@ -118,6 +118,24 @@ def time_calls(fns, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def topk_vs_torch(steps_, n):
+    """Selection kernel (msa_topk_blocks) against torch.topk(k=16, unsorted) on
+    the same block scores, back-to-back calls over the layers.  torch.topk does
+    not apply the method's rule (own block forced in, lower-index ties,
+    ascending output): this is a speed comparison only."""
+    import torch
+    for st in steps_:
+        st.score()
+    torch.cuda.synchronize()
+    k = steps_[0].cfg.topk
+    ours = time_calls([st.topk for st in steps_], n, 2)
+    theirs = time_calls([lambda st=st: torch.topk(st.scores, k, dim=-1, sorted=False)
+                         for st in steps_], n, 2)
+    rows = steps_[0].scores.shape[0] * steps_[0].scores.shape[1]
+    return {"rows": rows, "candidates_per_row": steps_[0].scores.shape[2],
+            "msa_topk_blocks_us": round(ours * 1e3, 2), "torch_topk_us": round(theirs * 1e3, 2)}
+
+
 def time_graph(steps_, steps, warmup):
     """Mean ms per layer-step when the layer-steps of all layers are captured as
     one HIP graph and the graph is replayed back to back."""
@@ -293,6 +311,7 @@ def main():
     # page kernel each move about half of the step's bytes)
     score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
     attn_ms = time_calls([s.attend for s in four], args.steps, args.warmup)
+    topk_line = {cfg.name: topk_vs_torch(four, args.steps)}
     layer_bytes = acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
 
     def frac(ms_):
@@ -364,6 +383,19 @@ def main():
         # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
         c5 = gen.config(5)
         also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4))
+        # multi-query decode: 4 draft tokens per sequence on the 60k workload,
+        # through msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill
+        import dataclasses
+        cm = dataclasses.replace(gen.config(2), name="multi_query_decode_b8_ctx60k_4drafts",
+                                 n_new=[4] * 8)
+        lm = make_layers(cm, 4)
+        sm = [MsaStep(x) for x in lm]
+        msm = time_calls([st.run for st in sm], max(20, args.steps // 4), 4)
+        also[cm.name] = {"us_per_layer_step": round(msm * 1e3, 2),
+                         "us_per_query_token": round(msm * 1e3 / cm.total_q, 2),
+                         "layers": 4}
+        del sm, lm
+        torch.cuda.empty_cache()
         # 1M-context decode, batch 4 (18 GB of K/V per layer): 2 layers
         c4 = gen.config(4)
         l4 = make_layers(c4, 2)
@@ -399,6 +431,8 @@ def main():
             "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
             "index_score_mfma_frac_of_measured": round(tf(fl_score, score3) / ceil["mfma_bf16_tflops"], 4),
             "attn_flops": fl_attn, "score_flops": fl_score}
+        topk_line[c3.name] = topk_vs_torch(s3, n3)
+        also["topk_vs_torch"] = topk_line
         del s3, l3
         torch.cuda.empty_cache()
         result["also"] = also

@@ -10,8 +10,9 @@
 //
 // Steps (all on the caller's stream):
 //   1. inverse map: histogram of (sequence, group, block) buckets over the
-//      selection, exclusive scan, scatter of (query, slot) entries;
-//   2. block-major attention: one workgroup per bucket stages the block's K
+//      selection, exclusive scan (which also lists the nonempty buckets),
+//      placement of (query, slot) entries;
+//   2. block-major attention: one workgroup per nonempty bucket stages the block's K
 //      and V (row-major, coalesced loads) in LDS once, then its wavefronts sweep
 //      the bucket's (query, head) rows 32 at a time with 32x32x16 bf16 matrix
 //      cores: S^T = K Q^T, row softmax in registers, P rounded to bf16 and
@@ -22,6 +23,8 @@
 //      output and an fp32 log-sum-exp;
 //   3. merge: per (query, head), the partials of its selected slots combine in
 //      slot order (deterministic; no float atomics).
+#include <algorithm>
+
 #include "msa_common.hpp"
 
 namespace msa {
@@ -49,6 +52,7 @@ __host__ __device__ inline int max_tiles(int total_q, int B, int Hkv) {
 struct PrefillWs {
     int32_t* counts;     // [NB] entries per (sequence, group, block) bucket
     int32_t* offsets;    // [NB + 1] exclusive scan of counts
+    int32_t* buckets;    // [NB + 1]: [0] = nonempty buckets, then their ids in order
     int32_t* tile_base;  // [max_tiles, maxblk] a tile's first position within a bucket
     int32_t* entries;    // [total_q * Hkv * k]: query << 4 | slot, grouped by bucket
     uint16_t* part_o;    // [total_q, Hq, k, 128] bf16
@@ -65,6 +69,8 @@ __host__ __device__ inline PrefillWs prefill_ws(void* base, int B, int Hkv, int 
     w.counts = reinterpret_cast<int32_t*>(p);
     p += align256(NB * 4);
     w.offsets = reinterpret_cast<int32_t*>(p);
+    p += align256((NB + 1) * 4);
+    w.buckets = reinterpret_cast<int32_t*>(p);
     p += align256((NB + 1) * 4);
     w.tile_base = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)max_tiles(total_q, B, Hkv) * maxblk * 4);
@@ -162,29 +168,47 @@ void bucket_count_kernel(const int32_t* __restrict__ sel, const int32_t* __restr
     }
 }
 
-// Exclusive scan of counts[0..n) into offsets[0..n], one workgroup.
+// Exclusive scan of counts[0..n) into offsets[0..n], one workgroup; it also
+// lists the nonempty buckets in order (buckets[0] = how many, then their
+// ids), so the attention kernel launches only as many workgroups as there can
+// be nonempty buckets and none walks an empty one.
 __global__ __launch_bounds__(1024)
-void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int n) {
+void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                 int32_t* __restrict__ buckets, int n) {
     __shared__ int part[1024];
+    __shared__ int partn[1024];
     const int tid = threadIdx.x;
     const int per = ceil_div(n, 1024);
     const int a = min(n, tid * per), e = min(n, a + per);
-    int sum = 0;
-    for (int i = a; i < e; ++i) sum += counts[i];
+    int sum = 0, ne = 0;
+    for (int i = a; i < e; ++i) {
+        const int c = counts[i];
+        sum += c;
+        ne += c > 0;
+    }
     part[tid] = sum;
+    partn[tid] = ne;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
         const int v = (tid >= off) ? part[tid - off] : 0;
+        const int vn = (tid >= off) ? partn[tid - off] : 0;
         __syncthreads();
         part[tid] += v;
+        partn[tid] += vn;
         __syncthreads();
     }
-    int run = part[tid] - sum;  // exclusive prefix of this thread's chunk
+    int run = part[tid] - sum;   // exclusive prefixes of this thread's chunk
+    int runn = partn[tid] - ne;
     for (int i = a; i < e; ++i) {
+        const int c = counts[i];
         offsets[i] = run;
-        run += counts[i];
+        run += c;
+        if (c > 0) buckets[1 + runn++] = i;
     }
-    if (tid == 1023) offsets[n] = part[1023];
+    if (tid == 1023) {
+        offsets[n] = part[1023];
+        buckets[0] = partn[1023];
+    }
 }
 
 // Pass 3: the tile places each selection at offsets[bucket] + its tile's base
@@ -226,9 +250,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // per-wave staging of 32 query rows in, then 32 partial-output rows out
     __shared__ __attribute__((aligned(16))) uint16_t tiles[(kPfThreads / kWave) * 32 * kKStride];
 
-    const int bk = blockIdx.x;
+    if ((int)blockIdx.x >= w.buckets[0]) return;  // uniform
+    const int bk = w.buckets[1 + blockIdx.x];
     const int cnt = w.counts[bk];
-    if (cnt == 0) return;
     const int base = w.offsets[bk];
     const int b = bk % maxblk;
     const int g = (bk / maxblk) % Hkv;
@@ -523,10 +547,12 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                        w.counts, NB);
     hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, NB);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, w.buckets, NB);
     hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
-    hipLaunchKernelGGL(block_major_kernel, dim3(NB), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
+    // at most one nonempty bucket per selection
+    const int n_bk = (int)std::min<int64_t>(NB, (int64_t)total_q * s.Hkv * kTopK);
+    hipLaunchKernelGGL(block_major_kernel, dim3(n_bk), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
                        block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
     const int nth = total_q * s.Hq * 16;

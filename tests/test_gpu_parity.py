@@ -34,6 +34,10 @@ SMALL = [
     # mixed: a sequence with no new tokens, one decode token, a prefill chunk
     gen.MsaConfig("mixed_batch", [4000, 900, 3000], [0, 1, 300], 12, 4, permute_pages=True,
                   seed=37),
+    # multi-query decode (speculative drafts): a few queries per sequence,
+    # scored by the per-block kernel and attended KV-block-major
+    gen.MsaConfig("multi_query_decode", [9000, 20000, 3000, 700], [4, 4, 2, 3], 12, 3,
+                  permute_pages=True, seed=48),
 ]
 
 
