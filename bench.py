@@ -20,8 +20,10 @@ kernel is timed the same way: K back-to-back calls of it over the layers.
 
 Also reported (``also``): decode at 4096 tokens (batch 1), ragged decode (16
 sequences, 4096 to 524,288 tokens), 1M-context decode (batch 4) with its
-scoring pass measured separately, and 8192-token chunked prefill onto a
-57,344-token prefix (tokens/s).  The headline layer-step is also timed as one
+scoring pass measured separately, 8192-token chunked prefill onto a
+57,344-token prefix (tokens/s), multi-query decode (4 drafts per sequence),
+the selection kernel against torch.topk, and the dense GQA decode baseline
+(msa_dense_attn_decode) at 60k and 1M with MSA's speedup over it.  The headline layer-step is also timed as one
 HIP graph per pass over the layers.  Roofline fractions are given against the
 published peaks and against ceilings measured in the same run
 (``measured_ceilings``: a streaming read and a matrix-core loop).  The
@@ -116,6 +118,32 @@ def time_calls(fns, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def dense_calls(xs):
+    """msa_dense_attn_decode (the dense GQA baseline) on each layer's inputs,
+    with its buffers allocated once."""
+    import torch
+    from block_sparse_attention_03_amd import _lib
+    fns = []
+    for x in xs:
+        d = _lib.dims_for(x.cfg)
+        ws = torch.empty(_lib.msa_dense_decode_workspace_size(d), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(x.q)
+        lse = torch.empty(x.q.shape[:2], dtype=torch.float32, device="cuda")
+        fns.append(lambda x=x, d=d, ws=ws, out=out, lse=lse: _lib.msa_dense_attn_decode(
+            d, x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, out, lse, ws))
+    return fns
+
+
+def dense_line(cfg, xs, n, msa_ms):
+    from block_sparse_attention_03_amd import accounting as acc
+    ms = time_calls(dense_calls(xs), n, 2)
+    nbytes = sum(cfg.seq_lens) * cfg.num_kv_heads * 4 * cfg.head_dim  # K and V, bf16
+    return {"us_per_layer_step": round(ms * 1e3, 2),
+            "kv_bytes": int(nbytes),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
+            "msa_speedup": round(ms / msa_ms, 2)}
 
 
 def topk_vs_torch(steps_, n):
@@ -312,6 +340,7 @@ def main():
     score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
     attn_ms = time_calls([s.attend for s in four], args.steps, args.warmup)
     topk_line = {cfg.name: topk_vs_torch(four, args.steps)}
+    dense = {cfg.name: dense_line(cfg, layers, max(16, args.steps // 8), fused_ms)}
     layer_bytes = acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
 
     def frac(ms_):
@@ -405,6 +434,7 @@ def main():
         ms4 = time_calls([s.run for s in f4], n4, 2)
         score4 = time_calls([s.score for s in s4], n4, 2)
         b4 = acc.score_bytes(c4) + acc.decode_attn_bytes(c4)
+        dense[c4.name] = dense_line(c4, l4, 6, ms4)
         also[c4.name] = {"us_per_layer_step": round(ms4 * 1e3, 2),
                          "layer_step_hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
                          "us_four_calls": round(time_calls([s.run for s in s4], n4, 2) * 1e3, 2),
@@ -433,6 +463,7 @@ def main():
             "attn_flops": fl_attn, "score_flops": fl_score}
         topk_line[c3.name] = topk_vs_torch(s3, n3)
         also["topk_vs_torch"] = topk_line
+        also["dense_gqa_decode"] = dense
         del s3, l3
         torch.cuda.empty_cache()
         result["also"] = also

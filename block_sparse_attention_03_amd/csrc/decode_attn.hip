@@ -18,23 +18,11 @@
 // the LDS transpose read.  Each page leaves a normalised partial
 // output and its log-sum-exp in the workspace; a second kernel merges a row's
 // pages with the Log-Sum-Exp rule (aivizor, KV-Block-Major paragraph).
+#include "decode_tile.hpp"
 #include "select.hpp"
 
 namespace msa {
 namespace {
-
-constexpr int kDecThreads = 256;
-// V sits in LDS as 128 rows (tokens) of 256 B, unpadded; the 16-byte chunk c
-// of token t is stored at chunk c ^ 2(t mod 8).  A transpose read takes the
-// same 32 B of 16 consecutive tokens, and the swizzle puts any 8 consecutive
-// tokens' copies of those 32 B on 8 disjoint sets of 8 banks, so the reads are
-// conflict-free; with no padding, four workgroups fit in a compute unit.
-__device__ __forceinline__ int vs_off(int t, int d) {  // bf16 offset of (token t, dim d)
-    return t * kHeadDim + ((((d >> 3) ^ ((t & 7) << 1))) << 3) + (d & 7);
-}
-constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 struct DecodeWs {
     float* o;    // [R, k, G, 128] normalised partial outputs
@@ -47,13 +35,6 @@ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
     w.lse = w.o + (size_t)R * kTopK * G * kHeadDim;
     return w;
 }
-
-struct DecodeShared {
-    uint16_t vs[kBlock * kHeadDim];
-    uint16_t pl[kMaxGroup * kPStride];
-    float red_max[4][kMaxGroup];
-    float red_sum[4][kMaxGroup];
-};
 
 // The G query heads of row r (sequence s, group g) against one page holding
 // nv valid tokens: writes the normalised partial output and log-sum-exp of

@@ -188,6 +188,33 @@ msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
                                            static_cast<hipStream_t>(stream)));
 }
 
+size_t msa_dense_decode_workspace_size(const msa_dims_t* dims) {
+    MsaShape s;
+    if (check_dims(dims, &s) != MSA_SUCCESS) return 0;
+    return msa_dense_decode_ws_bytes(s);
+}
+
+msa_status_t msa_dense_attn_decode(const msa_dims_t* dims, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   uint16_t* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    MsaShape s;
+    msa_status_t st = check_dims(dims, &s);
+    if (st != MSA_SUCCESS) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(out, 16) ||
+        (lse && !aligned(lse, 4)))
+        return MSA_ERROR_INVALID_VALUE;
+    if ((int64_t)s.B * s.Hkv > 65535) return MSA_ERROR_NOT_SUPPORTED;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < msa_dense_decode_ws_bytes(s))
+        return MSA_ERROR_WORKSPACE;
+    return launched(msa_launch_dense_decode(s, q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                                            workspace, static_cast<hipStream_t>(stream)));
+}
+
 const char* msa_status_string(msa_status_t status) {
     switch (status) {
         case MSA_SUCCESS: return "MSA_SUCCESS";

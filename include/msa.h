@@ -194,10 +194,28 @@ msa_status_t msa_decode_step(const msa_dims_t *dims, const uint16_t *q_idx,
                              float *lse, int32_t *sel, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * Dense GQA decode attention, the baseline MSA's decode speedup is measured
+ * against ([youmind] bullet "Rapido en produccion": decode vs dense GQA with
+ * the same heads): every query head of sequence s attends all seq_lens[s]
+ * cached tokens of its KV group, softmax(scale * q K^T) V.  Same caches and
+ * block table as the sparse path; one query per sequence at p = seq_lens[s]-1.
+ *   q     [B, H_q, 128] bf16; k_cache, v_cache, block_table, seq_lens as above
+ *   out   [B, H_q, 128] bf16 (output); lse [B, H_q] fp32 or NULL
+ *   workspace: at least msa_dense_decode_workspace_size(dims) bytes, 256-byte
+ *   aligned; no initial contents required.  seq_lens[s] >= 1.
+ */
+msa_status_t msa_dense_attn_decode(const msa_dims_t *dims, const uint16_t *q,
+                                   const uint16_t *k_cache, const uint16_t *v_cache,
+                                   const int32_t *block_table, const int32_t *seq_lens,
+                                   uint16_t *out, float *lse, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* Workspace sizes in bytes (0 for invalid dims). */
 size_t msa_decode_workspace_size(const msa_dims_t *dims);
 size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);
 size_t msa_decode_step_workspace_size(const msa_dims_t *dims);
+size_t msa_dense_decode_workspace_size(const msa_dims_t *dims);
 
 /* Static, human-readable name of a status code. */
 const char *msa_status_string(msa_status_t status);

@@ -112,6 +112,20 @@ def test_decode_and_prefill_workspace_errors():
     assert lib.msa_sparse_attn_prefill(ctypes.byref(d), 7, A, A, A, A, A, A, None, A, A, A, need_p, None) == L.MSA_ERROR_INVALID_VALUE
 
 
+def test_dense_decode_errors():
+    lib = L.lib()
+    d = dims()
+    need = L.msa_dense_decode_workspace_size(d)
+    assert need % 256 == 0 and need >= 4 * 3 * 4 * 129 * 4  # 4 rows, 10 blocks -> 3 chunks of 4, G = 4
+    assert L.msa_dense_decode_workspace_size(dims(head_dim=64)) == 0
+    assert lib.msa_dense_attn_decode(ctypes.byref(d), A, A, A, A, A, A, A, None, need, None) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_dense_attn_decode(ctypes.byref(d), A, A, A, A, A, A, A, A, need - 1, None) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_dense_attn_decode(ctypes.byref(d), None, A, A, A, A, A, A, A, need, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_dense_attn_decode(ctypes.byref(d), A, A, A, A, A, MIS, A, A, need, None) == L.MSA_ERROR_INVALID_VALUE
+    bad = dims(head_dim=64)
+    assert lib.msa_dense_attn_decode(ctypes.byref(bad), A, A, A, A, A, A, A, A, need, None) == L.MSA_ERROR_NOT_SUPPORTED
+
+
 def test_binding_checks_tensors_before_calling():
     import torch
     d = dims()

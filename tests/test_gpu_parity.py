@@ -267,3 +267,50 @@ def test_fused_decode_step_rows_past_8192_blocks():
             assert torch.equal(fused.sel, ref.sel)
         assert torch.equal(fused.out, ref.out)
         assert torch.equal(fused.lse, ref.lse)
+
+
+def _dense_decode(cfg, x):
+    d = L.dims_for(cfg)
+    ws = torch.empty(L.msa_dense_decode_workspace_size(d), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x.q)
+    lse = torch.empty((cfg.num_seqs, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    L.msa_dense_attn_decode(d, x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], SMALL[3], gen.config(1)], ids=lambda c: c.name)
+def test_dense_decode_baseline_matches_oracle(cfg):
+    """The dense GQA baseline attends every cached token: equal to the
+    oracle's fixed-page attention over each row's whole block table."""
+    import oracle
+    print(f"[dense] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    out, lse = _dense_decode(cfg, x)
+    H = cfg.num_kv_heads
+    pt = np.repeat(gen.bits(x.block_table), H, axis=0)
+    rl = np.repeat(np.asarray(cfg.seq_lens, dtype=np.int32), H)
+    ref_o, ref_l = oracle.paged_attention(gen.bits(x.q), gen.bits(x.k_cache), gen.bits(x.v_cache),
+                                          pt, rl)
+    got_o = out.float().cpu().numpy()
+    assert np.isfinite(got_o).all()
+    err = np.abs(got_o - ref_o)
+    lim = parity.OUT_ATOL + parity.OUT_RTOL * np.abs(ref_o)
+    assert (err <= lim).all(), f"out max abs err {err.max():.3g}"
+    assert np.abs(lse.cpu().numpy() - ref_l).max() <= parity.LSE_ATOL
+
+
+def test_dense_decode_equals_msa_when_every_block_is_selected():
+    """With k*Bk >= L every block is selected, so MSA's decode step and the
+    dense baseline compute the same attention (different partial splits:
+    equal within the output tolerance)."""
+    cfg = gen.MsaConfig("dense_vs_msa", [2048, 1500, 700, 130], [1] * 4, 16, 4,
+                        permute_pages=True, seed=49)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    msa = MsaStep(x, fused=True)
+    msa.run()
+    out, lse = _dense_decode(cfg, x)
+    err = (msa.out.float() - out.float()).abs()
+    lim = parity.OUT_ATOL + parity.OUT_RTOL * out.float().abs()
+    assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
+    assert (msa.lse - lse).abs().max().item() <= parity.LSE_ATOL
