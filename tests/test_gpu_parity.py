@@ -314,3 +314,55 @@ def test_dense_decode_equals_msa_when_every_block_is_selected():
     lim = parity.OUT_ATOL + parity.OUT_RTOL * out.float().abs()
     assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
     assert (msa.lse - lse).abs().max().item() <= parity.LSE_ATOL
+
+
+def test_decode_at_the_maximum_row_length():
+    """A decode row of 16384 blocks (2,097,152 tokens), the largest the ABI
+    accepts, next to a short one: full parity through the four calls, and the
+    fused step (which routes rows past 8192 blocks through the standalone
+    selection) equals them."""
+    cfg = gen.MsaConfig("decode_max_blocks", [16384 * 128, 5000], [1, 1], 2, 1,
+                        permute_pages=True, seed=50)
+    print(f"[max] maxblk={cfg.max_blocks}", flush=True)
+    assert cfg.max_blocks == 16384
+    x, step = parity.full_check(cfg, poison=True)
+    fused = MsaStep(x, fused=True)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.sel, step.sel)
+    assert torch.equal(fused.out, step.out)
+    assert torch.equal(fused.lse, step.lse)
+
+
+def test_fused_decode_step_graph_replay():
+    """msa_decode_step captured as one HIP graph: every replay, with eager work
+    and synchronisation between replays, equals the eager result bit for bit."""
+    cfg = gen.MsaConfig("graph_fused", [9000, 700, 140000], [1, 1, 1], 12, 4,
+                        permute_pages=True, seed=51)
+    x = gen.make_inputs(cfg, device="cuda")
+    step = MsaStep(x, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    ref_out, ref_lse, ref_sel = step.out.clone(), step.lse.clone(), step.sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    torch.cuda.synchronize()
+    for i in range(4):
+        step.out.zero_()
+        step.sel.fill_(-7)
+        step.run()
+        torch.cuda.synchronize()
+        step.out.zero_()
+        step.sel.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, ref_out), f"replay {i}: out differs"
+        assert torch.equal(step.lse, ref_lse), f"replay {i}: lse differs"
+        assert torch.equal(step.sel, ref_sel), f"replay {i}: sel differs"
