@@ -22,9 +22,11 @@ Also reported (``also``): decode at 4096 tokens (batch 1), ragged decode (16
 sequences, 4096 to 524,288 tokens), 1M-context decode (batch 4) with its
 scoring pass measured separately, 8192-token chunked prefill onto a
 57,344-token prefix (tokens/s), multi-query decode (4 drafts per sequence),
-the selection kernel against torch.topk, and the dense GQA decode baseline
-(msa_dense_attn_decode) at 60k and 1M with MSA's speedup over it.  The headline layer-step is also timed as one
-HIP graph per pass over the layers.  Roofline fractions are given against the
+the selection kernel against torch.topk, the dense GQA decode baseline
+(msa_dense_attn_decode) at 60k and 1M, and the dense causal prefill baseline
+(msa_dense_attn_prefill) on the 8192-token chunk, each with MSA's speedup over
+it.  The headline layer-step is also timed as one HIP graph per pass over the
+layers.  Roofline fractions are given against the
 published peaks and against ceilings measured in the same run
 (``measured_ceilings``: a streaming read and a matrix-core loop).  The
 oracle's CPU time on the headline workload is reported as ``cpu_baseline``.
@@ -461,6 +463,24 @@ def main():
             "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
             "index_score_mfma_frac_of_measured": round(tf(fl_score, score3) / ceil["mfma_bf16_tflops"], 4),
             "attn_flops": fl_attn, "score_flops": fl_score}
+        # dense causal prefill baseline on the same chunk
+        dfn = []
+        for x in l3:
+            d3 = _lib.dims_for(c3)
+            o3 = torch.empty_like(x.q)
+            e3 = torch.empty(x.q.shape[:2], dtype=torch.float32, device="cuda")
+            dfn.append(lambda x=x, d3=d3, o3=o3, e3=e3: _lib.msa_dense_attn_prefill(
+                d3, c3.total_q, x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.cu_q,
+                o3, e3))
+        dms3 = time_calls(dfn, max(4, n3 // 2), 1)
+        fl_dense = acc.dense_prefill_flops(c3)
+        also["dense_causal_prefill"] = {c3.name: {
+            "ms": round(dms3, 4), "flops": fl_dense,
+            "mfma_frac": round(tf(fl_dense, dms3) / acc.BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_of_measured": round(tf(fl_dense, dms3) / ceil["mfma_bf16_tflops"], 4),
+            "msa_step_speedup": round(dms3 / ms3, 2),
+            "msa_sparse_attn_call_speedup": round(dms3 / attn3, 2)}}
+        del dfn
         topk_line[c3.name] = topk_vs_torch(s3, n3)
         also["topk_vs_torch"] = topk_line
         also["dense_gqa_decode"] = dense

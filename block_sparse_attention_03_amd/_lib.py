@@ -27,7 +27,7 @@ EXPORTED = (
     "msa_index_score", "msa_topk_blocks", "msa_build_page_table", "msa_sparse_attn_decode",
     "msa_sparse_attn_prefill", "msa_decode_workspace_size", "msa_prefill_workspace_size",
     "msa_status_string", "msa_abi_version", "msa_decode_step", "msa_decode_step_workspace_size",
-    "msa_dense_attn_decode", "msa_dense_decode_workspace_size",
+    "msa_dense_attn_decode", "msa_dense_decode_workspace_size", "msa_dense_attn_prefill",
 )
 
 
@@ -75,11 +75,12 @@ def lib():
         L.msa_decode_step_workspace_size.argtypes = [D]
         L.msa_decode_step_workspace_size.restype = SZ
         L.msa_dense_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
+        L.msa_dense_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P]
         L.msa_dense_decode_workspace_size.argtypes = [D]
         L.msa_dense_decode_workspace_size.restype = SZ
         for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
                   "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_decode_step",
-                  "msa_dense_attn_decode"):
+                  "msa_dense_attn_decode", "msa_dense_attn_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_decode_workspace_size.argtypes = [D]
         L.msa_decode_workspace_size.restype = SZ
@@ -262,3 +263,19 @@ def msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out,
     nbytes = workspace.numel() if workspace is not None else 0
     _check(lib().msa_dense_attn_decode(ctypes.byref(d), *args, nbytes, _stream(stream)),
            "msa_dense_attn_decode")
+
+
+def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, out,
+                           lse, stream=None):
+    """Dense causal attention over every cached token (the prefill baseline)."""
+    d = dims
+    B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    args = (_ptr(q, BF16, "q", (total_q, Hq, d.head_dim)), _ptr(k_cache, BF16, "k_cache", cache),
+            _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
+            _ptr(out, BF16, "out", (total_q, Hq, d.head_dim)),
+            _ptr(lse, F32, "lse", (total_q, Hq)) if lse is not None else None)
+    _check(lib().msa_dense_attn_prefill(ctypes.byref(d), total_q, *args, _stream(stream)),
+           "msa_dense_attn_prefill")

@@ -55,6 +55,15 @@ def attn_flops(cfg) -> int:
     return sum(4 * cfg.head_dim * cfg.num_q_heads * n_att for _, n_att in _attended(cfg))
 
 
+def dense_prefill_flops(cfg) -> int:
+    """Dense causal baseline: the query at position p attends p + 1 tokens."""
+    n = 0
+    for L, q in zip(cfg.seq_lens, cfg.n_new):
+        # positions L-q .. L-1 attend L-q+1 .. L tokens
+        n += q * (L - q) + q * (q + 1) // 2
+    return 4 * cfg.head_dim * cfg.num_q_heads * n
+
+
 def prefill_attn_bytes(cfg) -> int:
     """KV-block-major prefill: each selected (sequence, group, block) K and V
     once, q read once per (query, head, slot), out + lse written, and the

@@ -239,3 +239,280 @@ hipError_t msa_launch_dense_decode(const MsaShape& s, const uint16_t* q, const u
                        lse, s.Hq, s.Hkv, R, chunk, chunks);
     return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Dense causal prefill: the baseline for MSA's chunked-prefill speedup
+// ---------------------------------------------------------------------------
+//
+// Query token t of sequence s (position p = L_s - nq_s + (t - q0_s)) attends
+// every cached token j <= p of its group.  One 256-thread workgroup owns 128
+// (query, head) rows of one (sequence, group) -- four 32-row tiles, one per
+// wavefront, rows ordered query-major with the group's G heads adjacent -- and
+// walks the KV blocks 0 .. (its last row's own block), staging each block's K
+// and V in LDS once for all its rows.  Per block and tile: S^T = K Q^T with
+// 32x32x16 bf16 products, the causal cut where a row's own block is reached,
+// the online softmax (running max and sum per row, accumulators rescaled),
+// P rounded to bf16 as the B operand of O^T += V^T P^T with V^T from LDS
+// transpose reads.  The staging tiles for the query gather and the output
+// store share the K/V region, so two workgroups fit in a compute unit: one
+// computes while the other stages.
+namespace msa {
+namespace {
+
+constexpr int kDpThreads = 256;
+constexpr int kDpRows = (kDpThreads / kWave) * 32;  // rows per workgroup
+constexpr int kDKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B)
+constexpr int kDVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B)
+
+struct DenseShared {
+    uint16_t ks[kBlock * kDKStride];
+    uint16_t vs[kBlock * kDVStride];
+};
+static_assert((kDpThreads / kWave) * 32 * kDKStride <= kBlock * kDKStride,
+              "query/output staging tiles fit in the K region");
+
+// Workgroup id -> (sequence, group, first row): sequence s has H_kv groups of
+// ceil(nq_s G / 128) row chunks each, dealt out in sequence order.  Lanes of
+// wavefront 0 scan 64 sequences at a time.  Returns false past the last one.
+__device__ bool dense_row_chunk(const int32_t* __restrict__ cu_q, int B, int Hkv, int G, int id,
+                                int* s_out, int* g_out, int* r0_out) {
+    const int lane = __lane_id();
+    int base = 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+        const int i = c0 + lane;
+        const int nq = (i < B) ? (cu_q[i + 1] - cu_q[i]) : 0;
+        const int per_group = ceil_div(nq * G, kDpRows);
+        const int n = per_group * Hkv;
+        int scan = n;  // inclusive prefix over lanes
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_up(scan, off, kWave);
+            if (lane >= off) scan += v;
+        }
+        const uint64_t hit = __ballot(base + scan > id);
+        if (hit) {
+            const int first = __builtin_ctzll(hit);
+            const int rem = id - base - __shfl(scan - n, first, kWave);
+            const int pg = __shfl(per_group, first, kWave);
+            *s_out = c0 + first;
+            *g_out = rem / pg;
+            *r0_out = (rem % pg) * kDpRows;
+            return true;
+        }
+        base += __shfl(scan, kWave - 1, kWave);
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(kDpThreads, 2)
+void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
+                          const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                          const uint16_t* __restrict__ v_cache,
+                          const int32_t* __restrict__ block_table,
+                          const int32_t* __restrict__ seq_lens,
+                          const int32_t* __restrict__ cu_q, uint16_t* __restrict__ out,
+                          float* __restrict__ lse_out, int B, int Hq, int Hkv, int maxblk,
+                          float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DenseShared sh;
+    __shared__ int info[3];
+    const int G = Hq / Hkv;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    if (wave == 0) {
+        int s_, g_, r0_;
+        const bool ok = dense_row_chunk(cu_q, B, Hkv, G, blockIdx.x, &s_, &g_, &r0_);
+        if (lane == 0) {
+            info[0] = ok ? s_ : -1;
+            info[1] = g_;
+            info[2] = r0_;
+        }
+    }
+    __syncthreads();
+    const int s = info[0];
+    if (s < 0) return;  // uniform
+    const int g = info[1];
+    const int q0 = cu_q[s];
+    const int nq = cu_q[s + 1] - q0;
+    const int L = seq_lens[s];
+    const int nrows = nq * G;
+    const int wg_row0 = info[2];
+    const int n = lane % 32;  // row of this lane within the wave's tile
+    const int h = lane / 32;  // lane half
+    uint16_t* tbuf = sh.ks + wave * 32 * kDKStride;  // staging tile (aliases K)
+
+    // this lane's row (rows past the sequence repeat its last row; results discarded)
+    const int rho0 = wg_row0 + wave * 32 + n;
+    const bool row_ok = rho0 < nrows;
+    const int rho = row_ok ? rho0 : nrows - 1;
+    const int t = q0 + rho / G;
+    const int head = g * G + rho % G;
+    const int p = L - nq + rho / G;
+    const int last_row = min(wg_row0 + kDpRows, nrows) - 1;
+    const int b_last = (L - nq + last_row / G) / kBlock;  // the workgroup's last block
+
+    // Q rows -> staging tile (coalesced 16-byte loads, 4 rows per instruction)
+    // -> B operands (k-step i of lane half h: dims 64h + 8i .. +7)
+    bf16x8 qb[8];
+    {
+        const int qrow = t * Hq + head;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int r = lane / 16 + 4 * it;
+            const size_t off = (size_t)__shfl(qrow, r, kWave) * kHeadDim;
+            *reinterpret_cast<u32x4*>(tbuf + r * kDKStride + 8 * (lane % 16)) =
+                ld16(q + off + 8 * (lane % 16));
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            qb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(tbuf + n * kDKStride + 64 * h + 8 * i));
+    }
+
+    float m_run = -__builtin_inff();  // running max of this lane's row, scaled log2 units
+    float l_run = 0.f;
+    f32x16 o_run[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o_run[mt] = f32x16{};
+    const int j = lane % 16;
+
+    for (int b = 0; b <= b_last; ++b) {
+        __syncthreads();  // previous block's reads (and the query staging) are done
+        {
+            const int nv = min(kBlock, L - b * kBlock);
+            const int page = block_table[(size_t)s * maxblk + b];
+            const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+            const uint16_t* kp = k_cache + page_off;
+            const uint16_t* vp = v_cache + page_off;
+            constexpr int kIt = kBlock * kHeadDim / 8 / kDpThreads;
+            u32x4 kv[kIt], vv[kIt];
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int c = tid + kDpThreads * it;
+                const int tok = c / 16, d0 = (c % 16) * 8;
+                kv[it] = (tok < nv) ? ld16(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+                vv[it] = (tok < nv) ? ld16(vp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int c = tid + kDpThreads * it;
+                const int tok = c / 16, d0 = (c % 16) * 8;
+                *reinterpret_cast<u32x4*>(sh.ks + tok * kDKStride + d0) = kv[it];
+                *reinterpret_cast<u32x4*>(sh.vs + tok * kDVStride + d0) = vv[it];
+            }
+        }
+        __syncthreads();
+
+        // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
+        // token 32mt + 8(v/4) + 4h + v%4 of row n
+        f32x16 sacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const uint16_t* krow = sh.ks + (32 * mt + n) * kDKStride + 64 * h;
+            sacc[mt] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                sacc[mt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * i)), qb[i], sacc[mt]);
+        }
+        // causal cut: token b*128 + tk visible iff <= p (all of a block before
+        // the row's own block is visible)
+        const int lim = p - b * kBlock;
+        if (__ballot(lim < kBlock - 1)) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tk = 32 * mt + 8 * (v / 4) + 4 * h + (v % 4);
+                    if (tk > lim) sacc[mt][v] = -__builtin_inff();
+                }
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[mt][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        // block 0 always holds token 0 <= p, so m_new is finite from the first block on
+        const float m_new = fmaxf(m_run, mx * scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on block 0
+
+        // P (bf16) as the B operand: k-step i covers tokens 16i..16i+15, i.e.
+        // accumulator values 8(i%2)..8(i%2)+7 of S^T tile i/2; the row sum uses
+        // the rounded weights the product uses
+        bf16x8 pb[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            u32x4 pw;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const float p0 = __builtin_amdgcn_exp2f(sacc[i / 2][8 * (i % 2) + 2 * e2] * scale_log2 - m_new);
+                const float p1 = __builtin_amdgcn_exp2f(sacc[i / 2][8 * (i % 2) + 2 * e2 + 1] * scale_log2 - m_new);
+                pw[e2] = pack2_bf16(p0, p1);
+                sum += bf16_lo(pw[e2]) + bf16_hi(pw[e2]);
+            }
+            pb[i] = as_bf16x8(pw);
+        }
+        sum += __shfl_xor(sum, 32, kWave);
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+
+        // O^T = alpha O^T + V^T P^T; dim tile mt: the A operand is the same
+        // tokens of dims 32mt + n from transpose reads of row-major V
+        const uint16_t* vsrc = sh.vs + (4 * h + j / 4) * kDVStride + 16 * ((lane / 16) % 2) + 4 * (j % 4);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x16 acc = o_run[mt] * alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x2 a0 = lds_read_tr16(vsrc + 16 * i * kDVStride + 32 * mt);
+                const u32x2 a1 = lds_read_tr16(vsrc + (16 * i + 8) * kDVStride + 32 * mt);
+                acc = mfma32(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb[i], acc);
+            }
+            o_run[mt] = acc;
+        }
+    }
+
+    // normalised output: O^T fragments -> staging tile (row n) -> coalesced
+    // 16-byte stores of 4 rows x 256 bytes per instruction
+    __syncthreads();  // every wave is done with the last block's K/V
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const int d = 32 * mt + 8 * qd + 4 * h;
+            *reinterpret_cast<u32x2*>(tbuf + n * kDKStride + d) =
+                u32x2{pack2_bf16(o_run[mt][4 * qd + 0] * inv, o_run[mt][4 * qd + 1] * inv),
+                      pack2_bf16(o_run[mt][4 * qd + 2] * inv, o_run[mt][4 * qd + 3] * inv)};
+        }
+    __builtin_amdgcn_wave_barrier();
+    const int orow = row_ok ? t * Hq + head : -1;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int r = lane / 16 + 4 * it;
+        const int o = __shfl(orow, r, kWave);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tbuf + r * kDKStride + 8 * (lane % 16));
+        if (o >= 0) *reinterpret_cast<u32x4*>(out + (size_t)o * kHeadDim + 8 * (lane % 16)) = v;
+    }
+    if (lse_out && row_ok && h == 0) lse_out[(size_t)t * Hq + head] = m_run * kLn2 + __logf(l_run);
+}
+
+}  // namespace
+}  // namespace msa
+
+hipError_t msa_launch_dense_prefill(const MsaShape& s, int total_q, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* cu_q, uint16_t* out, float* lse,
+                                    hipStream_t st) {
+    using namespace msa;
+    if (total_q == 0) return hipSuccess;
+    const int G = s.Hq / s.Hkv;
+    // upper bound on the row chunks: sum_s H_kv ceil(nq_s G / 128) <= H_kv (total_q G / 128 + B)
+    const int64_t chunks = (int64_t)s.Hkv * (ceil_div(total_q * G, kDpRows) + s.B);
+    hipLaunchKernelGGL(dense_prefill_kernel, dim3((unsigned)chunks), dim3(kDpThreads), 0, st, q,
+                       k_cache, v_cache, block_table, seq_lens, cu_q, out, lse, s.B, s.Hq, s.Hkv,
+                       s.maxblk, s.scale * kLog2e);
+    return hipGetLastError();
+}

@@ -215,6 +215,24 @@ msa_status_t msa_dense_attn_decode(const msa_dims_t* dims, const uint16_t* q,
                                             workspace, static_cast<hipStream_t>(stream)));
 }
 
+msa_status_t msa_dense_attn_prefill(const msa_dims_t* dims, int32_t total_q, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* cu_q, uint16_t* out, float* lse, void* stream) {
+    MsaShape s;
+    msa_status_t st = check_dims(dims, &s);
+    if (st != MSA_SUCCESS) return st;
+    if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_q || !out)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(cu_q, 4) ||
+        !aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return MSA_ERROR_INVALID_VALUE;
+    return launched(msa_launch_dense_prefill(s, total_q, q, k_cache, v_cache, block_table, seq_lens,
+                                             cu_q, out, lse, static_cast<hipStream_t>(stream)));
+}
+
 const char* msa_status_string(msa_status_t status) {
     switch (status) {
         case MSA_SUCCESS: return "MSA_SUCCESS";

@@ -155,6 +155,11 @@ hipError_t msa_launch_dense_decode(const MsaShape& s, const uint16_t* q, const u
                                    const uint16_t* v_cache, const int32_t* block_table,
                                    const int32_t* seq_lens, uint16_t* out, float* lse, void* ws,
                                    hipStream_t st);
+hipError_t msa_launch_dense_prefill(const MsaShape& s, int total_q, const uint16_t* q,
+                                    const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* cu_q, uint16_t* out, float* lse,
+                                    hipStream_t st);
 size_t msa_decode_step_ws_bytes(const MsaShape& s);
 hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, const uint16_t* kidx,
                                   const uint16_t* q, const uint16_t* k_cache,

@@ -211,6 +211,21 @@ msa_status_t msa_dense_attn_decode(const msa_dims_t *dims, const uint16_t *q,
                                    uint16_t *out, float *lse, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * Dense causal prefill attention, the baseline MSA's prefill speedup is
+ * measured against ([youmind] bullet "Rapido en produccion": prefill vs dense
+ * GQA with the same heads): query token t of sequence s (position
+ * p = seq_lens[s] - n_s + (t - cu_q[s])) attends every cached token j <= p of
+ * its KV group, softmax(scale * q K^T) V.  Same caches, block table and
+ * (cu_q, seq_lens) convention as msa_sparse_attn_prefill; no workspace.
+ *   q     [total_q, H_q, 128] bf16
+ *   out   [total_q, H_q, 128] bf16 (output); lse [total_q, H_q] fp32 or NULL
+ */
+msa_status_t msa_dense_attn_prefill(const msa_dims_t *dims, int32_t total_q, const uint16_t *q,
+                                    const uint16_t *k_cache, const uint16_t *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    const int32_t *cu_q, uint16_t *out, float *lse, void *stream);
+
 /* Workspace sizes in bytes (0 for invalid dims). */
 size_t msa_decode_workspace_size(const msa_dims_t *dims);
 size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);

@@ -126,6 +126,16 @@ def test_dense_decode_errors():
     assert lib.msa_dense_attn_decode(ctypes.byref(bad), A, A, A, A, A, A, A, A, need, None) == L.MSA_ERROR_NOT_SUPPORTED
 
 
+def test_dense_prefill_errors():
+    lib = L.lib()
+    d = dims()
+    assert lib.msa_dense_attn_prefill(ctypes.byref(d), 5, A, A, A, A, A, None, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_dense_attn_prefill(ctypes.byref(d), 5, MIS, A, A, A, A, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_dense_attn_prefill(ctypes.byref(d), -1, A, A, A, A, A, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    bad = dims(head_dim=64)
+    assert lib.msa_dense_attn_prefill(ctypes.byref(bad), 5, A, A, A, A, A, A, A, A, None) == L.MSA_ERROR_NOT_SUPPORTED
+
+
 def test_binding_checks_tensors_before_calling():
     import torch
     d = dims()

@@ -366,3 +366,78 @@ def test_fused_decode_step_graph_replay():
         assert torch.equal(step.out, ref_out), f"replay {i}: out differs"
         assert torch.equal(step.lse, ref_lse), f"replay {i}: lse differs"
         assert torch.equal(step.sel, ref_sel), f"replay {i}: sel differs"
+
+
+def _dense_prefill(cfg, x):
+    d = L.dims_for(cfg)
+    out = torch.empty_like(x.q)
+    lse = torch.empty((cfg.total_q, cfg.num_q_heads), dtype=torch.float32, device="cuda")
+    L.msa_dense_attn_prefill(d, cfg.total_q, x.q, x.k_cache, x.v_cache, x.block_table,
+                             x.seq_lens, x.cu_q, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _dense_prefill_oracle(cfg, x, tokens):
+    """Each sampled query token as a one-token row over its sequence's block
+    table, cut at its own position: dense causal attention by definition."""
+    import oracle
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    H = cfg.num_kv_heads
+    bt = gen.bits(x.block_table)
+    pt = np.repeat(bt[seq_of[tokens]], H, axis=0)
+    rl = np.repeat(pos_of[tokens] + 1, H).astype(np.int32)
+    q = gen.bits(x.q)[tokens]
+    return oracle.paged_attention(q, gen.bits(x.k_cache), gen.bits(x.v_cache), pt, rl)
+
+
+def _check_dense_prefill(cfg, x, out, lse, tokens):
+    ref_o, ref_l = _dense_prefill_oracle(cfg, x, tokens)
+    got_o = out.float().cpu().numpy()[tokens]
+    assert np.isfinite(got_o).all()
+    err = np.abs(got_o - ref_o)
+    lim = parity.OUT_ATOL + parity.OUT_RTOL * np.abs(ref_o)
+    assert (err <= lim).all(), f"out max abs err {err.max():.3g} (worst ratio {(err / lim).max():.3g})"
+    assert np.abs(lse.cpu().numpy()[tokens] - ref_l).max() <= parity.LSE_ATOL
+
+
+@pytest.mark.parametrize("cfg", [SMALL[4], SMALL[5], SMALL[6], SMALL[7],
+                                 gen.MsaConfig("dense_prefill_g16", [1000, 3000], [300, 1],
+                                               16, 1, permute_pages=True, seed=52)],
+                         ids=lambda c: c.name)
+def test_dense_prefill_baseline_matches_oracle(cfg):
+    """Every query token of the dense causal prefill baseline against the
+    oracle's attention over the whole prefix up to the token's position."""
+    print(f"[dense prefill] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    out, lse = _dense_prefill(cfg, x)
+    _check_dense_prefill(cfg, x, out, lse, np.arange(cfg.total_q))
+
+
+def test_dense_prefill_chunk_on_a_long_prefix_sampled():
+    """The 8192-token chunk on a 57,344-token prefix (48 query heads, 8 KV
+    heads): 14 sampled query tokens, among them the first and last of the
+    chunk, against the oracle."""
+    cfg = gen.config(3)
+    print(f"[dense prefill] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    out, lse = _dense_prefill(cfg, x)
+    rng = np.random.default_rng(7)
+    tokens = np.unique(np.concatenate([[0, 127, 128, cfg.total_q - 1],
+                                       rng.integers(0, cfg.total_q, 10)]))
+    _check_dense_prefill(cfg, x, out, lse, tokens)
+
+
+def test_dense_prefill_equals_msa_when_every_block_is_selected():
+    """Contexts of at most 16 blocks: MSA selects every block, so its
+    prefill and the dense baseline attend the same tokens."""
+    cfg = gen.MsaConfig("dense_vs_msa_prefill", [2048, 1500, 700], [700, 1, 130], 12, 3,
+                        permute_pages=True, seed=53)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    msa = MsaStep(x)
+    msa.run()
+    out, lse = _dense_prefill(cfg, x)
+    err = (msa.out.float() - out.float()).abs()
+    lim = parity.OUT_ATOL + parity.OUT_RTOL * out.float().abs()
+    assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
+    assert (msa.lse - lse).abs().max().item() <= parity.LSE_ATOL
