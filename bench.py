@@ -250,44 +250,62 @@ def recorded_traffic():
 
 
 def measured_ceilings():
-    """Sustained HBM read bandwidth (a 2 GiB streaming read) and bf16 matrix-core
-    rate (independent 32x32x16 products, 4 waves per SIMD) on this GPU, from the
-    separate calibration library."""
+    """Sustained HBM read bandwidth and bf16 matrix-core rate on this GPU, from
+    the separate calibration library: the best over a few grid sizes of a
+    2 GiB streaming read; the same for 64 MiB reads (the size of one decode
+    layer-step's two passes) cycling over 32 distinct slices; and independent
+    32x32x16 products at 4 and 8 waves per SIMD."""
     import ctypes
     import os
     import torch
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_sparse_attention_03_amd",
                         "libmsa_calib.so")
     c = ctypes.CDLL(path)
-    c.msa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                 ctypes.c_void_p]
+    c.msa_calib_read_grid.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     c.msa_calib_read_sink_len.restype = ctypes.c_size_t
     c.msa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     c.msa_calib_mfma_flop.restype = ctypes.c_double
     c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     nbytes = 2 << 30
+    small = 64 << 20
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.empty(c.msa_calib_read_sink_len(), dtype=torch.int32, device="cuda")
-    blocks, iters = 1024, 16384
-    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    iters = 16384
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
 
-    def read():
-        if c.msa_calib_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), st) != 0:
-            raise RuntimeError("msa_calib_read failed")
+    def read(ptr, size, grid):
+        if c.msa_calib_read_grid(ptr, size, grid, sink.data_ptr(), sink.numel(), st) != 0:
+            raise RuntimeError("msa_calib_read_grid failed")
 
-    def mfma():
+    def mfma(blocks):
         if c.msa_calib_mfma(out.data_ptr(), blocks, iters, st) != 0:
             raise RuntimeError("msa_calib_mfma failed")
 
-    read_ms = time_calls([read], 5, 2)
-    mfma_ms = time_calls([mfma], 3, 1)
+    big, sized = {}, {}
+    base = buf.data_ptr()
+    for grid in (256, 512, 1024, 4096):
+        ms = time_calls([lambda g=grid: read(base, nbytes, g)], 4, 1)
+        big[grid] = nbytes / (ms * 1e-3) / 1e9
+        fns = [lambda i=i, g=grid: read(base + i * small, small, g) for i in range(nbytes // small)]
+        ms = time_calls(fns, 2 * len(fns), len(fns))
+        sized[grid] = small / (ms * 1e-3) / 1e9
+    tflops = {}
+    for blocks in (1024, 2048):
+        ms = time_calls([lambda b=blocks: mfma(b)], 3, 1)
+        tflops[blocks] = c.msa_calib_mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
-    return {"hbm_read_gbs": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
-            "mfma_bf16_tflops": round(c.msa_calib_mfma_flop(blocks, iters) / (mfma_ms * 1e-3) / 1e12, 1),
-            "how": "2 GiB non-temporal streaming read; 32x32x16 bf16 MFMA loop, 4 independent "
-                   "chains per wave, 16 waves per CU"}
+    gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
+    return {"hbm_read_gbs": round(big[gb], 1),
+            "hbm_read_64mib_gbs": round(sized[gs], 1),
+            "mfma_bf16_tflops": round(tflops[bm], 1),
+            "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
+                   f"and of 64 MiB slices back to back (best grid {gs}); 32x32x16 bf16 MFMA "
+                   f"loop, 4 independent chains per wave, {bm // 256 * 4} waves per CU",
+            "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
+            "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
 
 
 def roofline_entry(name, nbytes, ms, traffic=None):
@@ -387,6 +405,8 @@ def main():
     result["measured_ceilings"] = ceil
     result["roofline"]["frac_of_measured"] = round(
         result["roofline"]["achieved"] / ceil["hbm_read_gbs"], 4)
+    result["roofline"]["frac_of_measured_64mib"] = round(
+        result["roofline"]["achieved"] / ceil["hbm_read_64mib_gbs"], 4)
     result["layer_step"]["hbm_frac_of_measured"] = round(
         result["layer_step"]["hbm_frac"] * acc.HBM_PEAK_GBS / ceil["hbm_read_gbs"], 4)
 

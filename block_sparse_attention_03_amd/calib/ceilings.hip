@@ -78,6 +78,19 @@ int msa_calib_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_le
     return (int)hipGetLastError();
 }
 
+// The same read with `blocks` workgroups (1 .. msa_calib_read_blocks()), for
+// reads of a few tens of MB where the grid size sets how fast the chip fills.
+int msa_calib_read_grid(const void* buf, size_t bytes, int blocks, uint32_t* sink, size_t sink_len,
+                        void* stream) {
+    if (!buf || !sink || bytes % 16 != 0 || blocks <= 0 || blocks > msa_calib_read_blocks() ||
+        sink_len < msa_calib_read_sink_len())
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), bytes / 16,
+                       sink);
+    return (int)hipGetLastError();
+}
+
 // bf16 FLOP of one msa_calib_mfma launch of `blocks` workgroups.
 double msa_calib_mfma_flop(int blocks, int iters) {
     return (double)blocks * (kThreads / 64) * iters * 4 * (32.0 * 32.0 * 16.0 * 2.0);

@@ -26,6 +26,8 @@
 // the A-operand reads are bank-conflict free) and used by all 8 wavefronts.
 // The epilogue masks tokens past each row's position and keeps per-row block
 // maxima in registers, so the 32x32 products never leave the chip.
+#include <type_traits>
+
 #include "msa_common.hpp"
 
 namespace msa {
@@ -193,9 +195,11 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
         }
     }
     __syncthreads();
-    const int s = grp[0];
-    if (s < 0) return;  // workgroup-uniform
-    const int rg = grp[1];
+    // workgroup-uniform: kept in scalar registers so that every test derived
+    // from them is a scalar branch
+    const int s = __builtin_amdgcn_readfirstlane(grp[0]);
+    if (s < 0) return;
+    const int rg = __builtin_amdgcn_readfirstlane(grp[1]);
     const int L = seq_lens[s];
     const int q0 = cu_q[s];
     const int nq = cu_q[s + 1] - q0;
@@ -263,38 +267,50 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
     __syncthreads();
 
     // Block b from LDS buffer buf: per-row maxima over this lane half's tokens.
-    auto do_block = [&](int b, int buf, float (&mx)[kGTiles]) {
-#pragma unroll
-        for (int r = 0; r < kGTiles; ++r) mx[r] = -__builtin_inff();
-        if (b >= b_vis_end) return;  // workgroup-uniform
-        const unsigned char* kt = ktile[buf];
-        const int tok_base = b * kBlock;
-        const bool need_mask = tok_base + kBlock - 1 > p_first;
+    // Per 32-token tile the four row tiles' products are independent chains,
+    // issued interleaved; their maxima are taken after the last product.
+    // Only blocks that reach past the group's first position need the causal
+    // mask (a workgroup-uniform choice made once per block).
+    auto block_body = [&](const unsigned char* kt, int tok_base, float (&mx)[kGTiles], auto masked) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             bf16x8 a[4];
             const unsigned char* arow = kt + (32 * tt + n) * kKStrideB + 64 * h;
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * i));
+            f32x16 acc[kGTiles];
+#pragma unroll
+            for (int r = 0; r < kGTiles; ++r) acc[r] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < kGTiles; ++r) acc[r] = mfma32(a[i], qb[r][i], acc[r]);
 #pragma unroll
             for (int r = 0; r < kGTiles; ++r) {
-                f32x16 acc = {};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma32(a[i], qb[r][i], acc);
                 float m = -__builtin_inff();
-                if (need_mask) {
+                if constexpr (decltype(masked)::value) {
                     // value v is token tok_base + 32tt + 8(v/4) + 4h + v%4 of row n
                     const int lim = prow[r] - tok_base - 32 * tt - 4 * h;
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[v] : -__builtin_inff());
+                        m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[r][v] : -__builtin_inff());
                 } else {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[v]);
+                    for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[r][v]);
                 }
                 mx[r] = fmaxf(mx[r], m);
             }
         }
+    };
+    auto do_block = [&](int b, int buf, float (&mx)[kGTiles]) {
+#pragma unroll
+        for (int r = 0; r < kGTiles; ++r) mx[r] = -__builtin_inff();
+        if (b >= b_vis_end) return;  // workgroup-uniform
+        const int tok_base = b * kBlock;
+        if (tok_base + kBlock - 1 > p_first)
+            block_body(ktile[buf], tok_base, mx, std::true_type{});
+        else
+            block_body(ktile[buf], tok_base, mx, std::false_type{});
     };
 
     for (int b0 = b_begin, cur = 0; b0 < b_end; b0 += 2, cur ^= 2) {

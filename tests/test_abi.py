@@ -142,3 +142,20 @@ def test_binding_checks_tensors_before_calling():
     cpu = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         L.msa_index_score(d, 4, cpu, cpu, cpu, cpu, cpu, cpu)
+
+
+def test_calibration_library_exports():
+    """The benchmark's measured-ceiling kernels live in a separate library."""
+    import os
+    path = os.path.join(os.path.dirname(L.LIB_PATH), "libmsa_calib.so")
+    c = ctypes.CDLL(path)
+    for name in ("msa_calib_read_blocks", "msa_calib_read_sink_len", "msa_calib_read",
+                 "msa_calib_read_grid", "msa_calib_mfma_flop", "msa_calib_mfma"):
+        assert hasattr(c, name), name
+    c.msa_calib_mfma_flop.restype = ctypes.c_double
+    c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert c.msa_calib_mfma_flop(2, 3) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2
+    c.msa_calib_read_grid.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    # argument errors are caught before any launch
+    assert c.msa_calib_read_grid(None, 16, 4, None, 0, None) != 0
