@@ -136,6 +136,8 @@ constexpr int kGTiles = 4;                       // 32-row tiles per wavefront
 constexpr int kGRows = kGWaves * kGTiles * 32;   // rows per workgroup (1024)
 constexpr int kGBlocks = 64;                     // blocks per workgroup chunk
 constexpr int kKStrideB = kIdxDim * 2 + 16;      // bytes per LDS index-key row (padded)
+constexpr int kStageBlocks = 16;                 // block maxima staged per row before a flush
+constexpr int kStageStride = kStageBlocks + 1;   // floats per staged row (padded)
 // s_waitcnt immediate: vector-memory count 0, the other counters unconstrained
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -179,6 +181,9 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
                              float* __restrict__ scores,           // [T, Hkv, maxblk]
                              int B, int Hkv, int Hidx, int maxblk) {
     __shared__ __attribute__((aligned(16))) unsigned char ktile[4][kBlock * kKStrideB];
+    // per-row block maxima of the current 16 blocks: each row's scores leave
+    // as one 64-byte run instead of 8-byte pieces every second block
+    __shared__ float stage[kGRows * kStageStride];
     __shared__ int grp[2];
 
     const int tid = threadIdx.x;
@@ -313,6 +318,24 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
             block_body(ktile[buf], tok_base, mx, std::false_type{});
     };
 
+    // This wavefront's 128 rows of the stage -> scores[.., fb .. fb + cnt - 1]:
+    // 16 lanes per row, four rows per store instruction.  Row rho of the
+    // group is score row (q0 + rho / R) * H_kv + g, i.e. q0 H_kv + rho when
+    // one index head serves every group (R = H_kv), else (q0 + rho) H_kv + ih.
+    const int wrow0 = wave * kGTiles * 32;  // first stage row of this wavefront
+    auto flush = [&](int fb, int cnt) {
+        const int col = lane % kStageBlocks;
+#pragma unroll 4
+        for (int k = 0; k < kGTiles * 32 * kStageBlocks / kWave; ++k) {
+            const int rl = wrow0 + lane / kStageBlocks + (kWave / kStageBlocks) * k;
+            const int rho = row0 + rl;
+            if (col < cnt && rho < row_end) {
+                const size_t srow = (Hidx == 1) ? (size_t)q0 * Hkv + rho : (size_t)(q0 + rho) * Hkv + ih;
+                scores[srow * maxblk + fb + col] = stage[rl * kStageStride + col];
+            }
+        }
+    };
+
     for (int b0 = b_begin, cur = 0; b0 < b_end; b0 += 2, cur ^= 2) {
         if (b0 + 2 < b_vis_end) load_tile(b0 + 2, stage0);
         if (b0 + 3 < b_vis_end) load_tile(b0 + 3, stage1);
@@ -320,17 +343,18 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
         do_block(b0, cur, m0);
         do_block(b0 + 1, cur + 1, m1);
         // both lane halves saw different tokens of the same row: combine, then
-        // half h writes block b0 + h
+        // half h stages block b0 + h (a wavefront reads back only its own rows,
+        // in order, so no barrier is needed before the flush)
+        const int j = (b0 - b_begin) % kStageBlocks;
 #pragma unroll
         for (int r = 0; r < kGTiles; ++r) {
             m0[r] = fmaxf(m0[r], __shfl_xor(m0[r], 32, kWave));
             m1[r] = fmaxf(m1[r], __shfl_xor(m1[r], 32, kWave));
-            const int b = b0 + h;
-            if (!rok[r] || b >= b_end) continue;
-            const int rho = row0 + (wave * kGTiles + r) * 32 + n;
-            const int t = q0 + rho / R;
-            const int g = (Hidx == 1) ? rho % R : ih;
-            scores[((size_t)t * Hkv + g) * maxblk + b] = h ? m1[r] : m0[r];
+            stage[(wrow0 + r * 32 + n) * kStageStride + j + h] = h ? m1[r] : m0[r];
+        }
+        if (j + 2 == kStageBlocks || b0 + 2 >= b_end) {
+            const int fb = b0 - j;
+            flush(fb, min(kStageBlocks, b_end - fb));
         }
         // buffers cur ^ 2, (cur ^ 2) + 1 were last read in the previous pair,
         // which every wavefront finished before that pair's barrier
