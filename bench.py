@@ -286,14 +286,15 @@ def measured_ceilings():
     big, sized = {}, {}
     base = buf.data_ptr()
     for grid in (256, 512, 1024, 4096):
-        ms = time_calls([lambda g=grid: read(base, nbytes, g)], 4, 1)
+        ms = time_calls([lambda g=grid: read(base, nbytes, g)], 6, 2)
         big[grid] = nbytes / (ms * 1e-3) / 1e9
         fns = [lambda i=i, g=grid: read(base + i * small, small, g) for i in range(nbytes // small)]
         ms = time_calls(fns, 2 * len(fns), len(fns))
         sized[grid] = small / (ms * 1e-3) / 1e9
     tflops = {}
     for blocks in (1024, 2048):
-        ms = time_calls([lambda b=blocks: mfma(b)], 3, 1)
+        # enough warm-up launches (about 1 ms each) for the clocks to settle
+        ms = time_calls([lambda b=blocks: mfma(b)], 10, 5)
         tflops[blocks] = c.msa_calib_mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
