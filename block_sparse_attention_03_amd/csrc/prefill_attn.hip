@@ -21,10 +21,16 @@
 //      next row tile's query gathers are issued before the current tile's
 //      softmax, hiding their latency.  Each (query, head, slot) gets a normalised bf16 partial
 //      output and an fp32 log-sum-exp;
+//      Buckets of at most 32 (query, head) rows -- a few queries per sequence,
+//      as in multi-query decode -- go to a lighter kernel instead: 256
+//      threads, each wavefront's 32 tokens of K held as 16x16x32 A operands,
+//      V in a swizzled unpadded LDS tile, the rows 16 at a time, so that four
+//      workgroups share a compute unit and the page loads overlap;
 //   3. merge: per (query, head), the partials of its selected slots combine in
 //      slot order (deterministic; no float atomics).
 #include <algorithm>
 
+#include "decode_tile.hpp"
 #include "msa_common.hpp"
 
 namespace msa {
@@ -35,8 +41,8 @@ constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-byt
                                          // consecutive rows hit distinct banks)
 constexpr int kVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B: the transpose reads
                                          // of 4 consecutive rows x 64 B hit distinct banks)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+// Buckets of at most this many (query, head) rows take the small-bucket kernel.
+constexpr int kSmallRows = 32;
 
 // Inverse-map tiles: the selections of one KV group over kTileTokens
 // consecutive query tokens of one sequence.
@@ -52,7 +58,8 @@ __host__ __device__ inline int max_tiles(int total_q, int B, int Hkv) {
 struct PrefillWs {
     int32_t* counts;     // [NB] entries per (sequence, group, block) bucket
     int32_t* offsets;    // [NB + 1] exclusive scan of counts
-    int32_t* buckets;    // [NB + 1]: [0] = nonempty buckets, then their ids in order
+    int32_t* buckets;    // [NB + 1]: [0] = buckets of more than kSmallRows rows, then their ids
+    int32_t* small;      // [NB + 1]: [0] = nonempty buckets of at most kSmallRows rows, then ids
     int32_t* tile_base;  // [max_tiles, maxblk] a tile's first position within a bucket
     int32_t* entries;    // [total_q * Hkv * k]: query << 4 | slot, grouped by bucket
     uint16_t* part_o;    // [total_q, Hq, k, 128] bf16
@@ -71,6 +78,8 @@ __host__ __device__ inline PrefillWs prefill_ws(void* base, int B, int Hkv, int 
     w.offsets = reinterpret_cast<int32_t*>(p);
     p += align256((NB + 1) * 4);
     w.buckets = reinterpret_cast<int32_t*>(p);
+    p += align256((NB + 1) * 4);
+    w.small = reinterpret_cast<int32_t*>(p);
     p += align256((NB + 1) * 4);
     w.tile_base = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)max_tiles(total_q, B, Hkv) * maxblk * 4);
@@ -169,45 +178,72 @@ void bucket_count_kernel(const int32_t* __restrict__ sel, const int32_t* __restr
 }
 
 // Exclusive scan of counts[0..n) into offsets[0..n], one workgroup; it also
-// lists the nonempty buckets in order (buckets[0] = how many, then their
-// ids), so the attention kernel launches only as many workgroups as there can
-// be nonempty buckets and none walks an empty one.
+// lists the nonempty buckets in order, those of more than small_cnt entries in
+// buckets and the others in small ([0] = how many, then their ids), so each
+// attention kernel launches only as many workgroups as there can be buckets
+// and none walks an empty one.
 __global__ __launch_bounds__(1024)
 void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                 int32_t* __restrict__ buckets, int n) {
+                 int32_t* __restrict__ buckets, int32_t* __restrict__ small, int n,
+                 int small_cnt) {
     __shared__ int part[1024];
-    __shared__ int partn[1024];
+    __shared__ int partl[1024];
+    __shared__ int parts[1024];
     const int tid = threadIdx.x;
     const int per = ceil_div(n, 1024);
     const int a = min(n, tid * per), e = min(n, a + per);
-    int sum = 0, ne = 0;
-    for (int i = a; i < e; ++i) {
-        const int c = counts[i];
-        sum += c;
-        ne += c > 0;
+    // counts are read eight at a time, so that a thread's chunk costs one
+    // memory round trip per eight buckets rather than one per bucket
+    constexpr int kBatch = 8;
+    int sum = 0, nl = 0, ns = 0;
+    for (int i0 = a; i0 < e; i0 += kBatch) {
+        int c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = (i0 + u < e) ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            sum += c[u];
+            nl += c[u] > small_cnt;
+            ns += c[u] > 0 && c[u] <= small_cnt;
+        }
     }
     part[tid] = sum;
-    partn[tid] = ne;
+    partl[tid] = nl;
+    parts[tid] = ns;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
         const int v = (tid >= off) ? part[tid - off] : 0;
-        const int vn = (tid >= off) ? partn[tid - off] : 0;
+        const int vl = (tid >= off) ? partl[tid - off] : 0;
+        const int vs = (tid >= off) ? parts[tid - off] : 0;
         __syncthreads();
         part[tid] += v;
-        partn[tid] += vn;
+        partl[tid] += vl;
+        parts[tid] += vs;
         __syncthreads();
     }
     int run = part[tid] - sum;   // exclusive prefixes of this thread's chunk
-    int runn = partn[tid] - ne;
-    for (int i = a; i < e; ++i) {
-        const int c = counts[i];
-        offsets[i] = run;
-        run += c;
-        if (c > 0) buckets[1 + runn++] = i;
+    int runl = partl[tid] - nl;
+    int runs = parts[tid] - ns;
+    for (int i0 = a; i0 < e; i0 += kBatch) {
+        int c[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) c[u] = (i0 + u < e) ? counts[i0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (i0 + u < e) {
+                offsets[i0 + u] = run;
+                run += c[u];
+                if (c[u] > small_cnt)
+                    buckets[1 + runl++] = i0 + u;
+                else if (c[u] > 0)
+                    small[1 + runs++] = i0 + u;
+            }
+        }
     }
     if (tid == 1023) {
         offsets[n] = part[1023];
-        buckets[0] = partn[1023];
+        buckets[0] = partl[1023];
+        small[0] = parts[1023];
     }
 }
 
@@ -471,6 +507,160 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     }
 }
 
+// Small buckets (at most kSmallRows (query, head) rows): one 256-thread
+// workgroup per bucket.  Each wavefront holds its 32 tokens of K as 16x16x32
+// A operands straight from HBM; V goes to the swizzled LDS tile; the rows go
+// 16 at a time as B-operand columns: S^T = K Q^T, a per-row causal cut, the
+// row max and sum across the four wavefronts through LDS, P (bf16) through
+// LDS, O^T = V^T P^T with each wavefront owning 32 dims.  Partial outputs and
+// log-sum-exps go where the block-major kernel puts them.
+__global__ __launch_bounds__(kDecThreads)
+void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
+                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                         const uint16_t* __restrict__ v_cache,
+                         const int32_t* __restrict__ block_table,
+                         const int32_t* __restrict__ seq_lens,
+                         const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
+                         int maxblk, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    if ((int)blockIdx.x >= w.small[0]) return;  // uniform
+    const int bk = w.small[1 + blockIdx.x];
+    const int cnt = w.counts[bk];
+    const int base = w.offsets[bk];
+    const int b = bk % maxblk;
+    const int g = (bk / maxblk) % Hkv;
+    const int s = bk / (maxblk * Hkv);
+    const int G = Hq / Hkv;
+    const int L = seq_lens[s];
+    const int nq = cu_q[s + 1] - cu_q[s];
+    const int pos0 = L - nq - cu_q[s];  // p = pos0 + t
+    const int nv = min(kBlock, L - b * kBlock);
+    const int page = block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    const uint16_t* kp = k_cache + page_off;
+    const uint16_t* vp = v_cache + page_off;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int n = lane % 16;   // row (B / result column) or row of A
+    const int kg = lane / 16;  // lane group
+
+    // V -> LDS (tokens at or past nv are zero), K -> A operands of this
+    // wavefront's tokens 32w + 16j + n, dims 32i + 8kg
+    {
+        u32x4 vv[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int tok = tid / 16 + 16 * it;
+            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+            *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
+    }
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 32 * wave + 16 * j + n;
+            ka[j][i] = as_bf16x8(tok < nv ? ld16_stream(kp + tok * kHeadDim + 32 * i + 8 * kg)
+                                          : u32x4{0u, 0u, 0u, 0u});
+        }
+
+    const int nrows = cnt * G;
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+        // row n of this group: its query, head and slot (rows past the bucket
+        // repeat its last row; their results are discarded)
+        const int rho0 = r0 + n;
+        const bool row_ok = rho0 < nrows;
+        const int rho = row_ok ? rho0 : nrows - 1;
+        const int entry = w.entries[base + rho / G];
+        const int t = entry >> 4;
+        const int slot = entry & 15;
+        const int head = g * G + rho % G;
+        bf16x8 qb[4];
+        const uint16_t* qrow = q + ((size_t)t * Hq + head) * kHeadDim;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb[i] = as_bf16x8(ld16(qrow + 32 * i + 8 * kg));
+        __syncthreads();  // V staged (first group) / the previous group's LDS reads done
+
+        // S^T for tokens 32w + 16j + 4kg + rr of row n; a token is visible iff
+        // it is in the cache (< nv) and at or before the row's position
+        const int lim = min(nv - 1, pos0 + t - b * kBlock);
+        f32x4 sacc[2];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[j] = mfma16(ka[j][i], qb[i], sacc[j]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int tok = 32 * wave + 16 * j + 4 * kg + rr;
+                if (tok > lim) sacc[j][rr] = -__builtin_inff();
+                mx = fmaxf(mx, sacc[j][rr]);
+            }
+        }
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);
+        if (kg == 0) sh.red_max[wave][n] = mx;
+        __syncthreads();
+        const float m = fmaxf(fmaxf(sh.red_max[0][n], sh.red_max[1][n]),
+                              fmaxf(sh.red_max[2][n], sh.red_max[3][n]));
+        // P rounded to bf16; the sum uses the rounded weights
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int tok = 32 * wave + 16 * j + 4 * kg;
+            uint32_t pw[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const float p0 = __builtin_amdgcn_exp2f((sacc[j][2 * e2] - m) * scale_log2);
+                const float p1 = __builtin_amdgcn_exp2f((sacc[j][2 * e2 + 1] - m) * scale_log2);
+                pw[e2] = pack2_bf16(p0, p1);
+                sum += bf16_lo(pw[e2]) + bf16_hi(pw[e2]);
+            }
+            *reinterpret_cast<u32x2*>(sh.pl + n * kPStride + tok) = u32x2{pw[0], pw[1]};
+        }
+        sum += __shfl_xor(sum, 16, kWave);
+        sum += __shfl_xor(sum, 32, kWave);
+        if (kg == 0) sh.red_sum[wave][n] = sum;
+        __syncthreads();
+
+        // O^T = V^T P^T for dims 32w .. 32w+31; k-step ks covers tokens
+        // 32ks + 4kg + 0..3 and 32ks + 16 + 4kg + 0..3
+        f32x4 oacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ta = 32 * ks + 4 * kg;
+            const u32x2 p0 = *reinterpret_cast<const u32x2*>(sh.pl + n * kPStride + ta);
+            const u32x2 p1 = *reinterpret_cast<const u32x2*>(sh.pl + n * kPStride + ta + 16);
+            const bf16x8 pbv = as_bf16x8(u32x4{p0[0], p0[1], p1[0], p1[1]});
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint16_t* src = sh.vs + vs_off(ta + n / 4, 32 * wave + 16 * mt + 4 * (n % 4));
+                const u32x2 v0a = lds_read_tr16(src);
+                const u32x2 v1a = lds_read_tr16(src + 16 * kHeadDim);
+                oacc[mt] = mfma16(as_bf16x8(u32x4{v0a[0], v0a[1], v1a[0], v1a[1]}), pbv, oacc[mt]);
+            }
+        }
+        const float l = sh.red_sum[0][n] + sh.red_sum[1][n] + sh.red_sum[2][n] + sh.red_sum[3][n];
+        if (row_ok) {
+            const size_t prow = ((size_t)t * Hq + head) * kTopK + slot;
+            const float inv = 1.0f / l;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int d = 32 * wave + 16 * mt + 4 * kg;
+                *reinterpret_cast<u32x2*>(w.part_o + prow * kHeadDim + d) =
+                    u32x2{pack2_bf16(oacc[mt][0] * inv, oacc[mt][1] * inv),
+                          pack2_bf16(oacc[mt][2] * inv, oacc[mt][3] * inv)};
+            }
+            if (wave == 0 && kg == 0) w.part_lse[prow] = m * scale_log2 * kLn2 + __logf(l);
+        }
+    }
+}
+
 // 16 threads per (query, head), 8 dims each: merge the selected slots' partials.
 __global__ __launch_bounds__(256)
 void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
@@ -547,13 +737,18 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                        w.counts, NB);
     hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, w.buckets, NB);
+    const int G = s.Hq / s.Hkv;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, w.buckets,
+                       w.small, NB, kSmallRows / G);
     hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
     // at most one nonempty bucket per selection
     const int n_bk = (int)std::min<int64_t>(NB, (int64_t)total_q * s.Hkv * kTopK);
     hipLaunchKernelGGL(block_major_kernel, dim3(n_bk), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
                        block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
+                       s.scale * kLog2e);
+    hipLaunchKernelGGL(bucket_small_kernel, dim3(n_bk), dim3(kDecThreads), 0, st, q, k_cache,
+                       v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
     const int nth = total_q * s.Hq * 16;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,

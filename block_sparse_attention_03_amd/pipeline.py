@@ -14,14 +14,16 @@ from . import _lib as L
 
 
 class MsaStep:
-    def __init__(self, x, lse: bool = True, fused: bool = False):
+    def __init__(self, x, lse: bool = True, fused: bool = False, prefill: bool = False):
+        """fused: the decode step as one msa_decode_step call; prefill: take the
+        prefill entry point even when every sequence has a single query."""
         cfg = x.cfg
         self.x = x
         self.cfg = cfg
         self.dims = L.dims_for(cfg)
         dev = x.q.device
         T, H, W = cfg.total_q, cfg.num_kv_heads, cfg.max_blocks
-        self.decode = cfg.is_decode
+        self.decode = cfg.is_decode and not prefill
         self.scores = torch.empty((T, H, W), dtype=torch.float32, device=dev)
         self.sel = torch.empty((T, H, cfg.topk), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)

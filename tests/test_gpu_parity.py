@@ -441,3 +441,40 @@ def test_dense_prefill_equals_msa_when_every_block_is_selected():
     lim = parity.OUT_ATOL + parity.OUT_RTOL * out.float().abs()
     assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
     assert (msa.lse - lse).abs().max().item() <= parity.LSE_ATOL
+
+
+@pytest.mark.parametrize("cfg", [
+    # G = 6: buckets of up to 5 queries (30 rows, two 16-row groups) take the
+    # small-bucket kernel; the drafts' shared own block holds 5 or 6 queries
+    gen.MsaConfig("mq_g6_5drafts", [9000, 20000, 4100], [5, 6, 5], 48, 8, permute_pages=True,
+                  seed=54),
+    # G = 16: at most 2 queries (32 rows) per small bucket
+    gen.MsaConfig("mq_g16_3drafts", [7000, 3000], [3, 2], 16, 1, permute_pages=True, seed=55),
+], ids=lambda c: c.name)
+def test_small_and_large_buckets(cfg):
+    """Few queries per sequence split the (sequence, group, block) buckets
+    between the small-bucket kernel and the block-major kernel; every output
+    row against the oracle."""
+    print(f"[buckets] {cfg.name}", flush=True)
+    parity.full_check(cfg, poison=True)
+
+
+def test_prefill_entry_with_one_query_per_sequence():
+    """Single-query sequences through msa_sparse_attn_prefill (every bucket
+    small): equal to the oracle, and to the decode path's attention."""
+    cfg = gen.MsaConfig("prefill_entry_one_query", [5000, 700, 12000], [1, 1, 1], 12, 4,
+                        permute_pages=True, seed=56)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    step = MsaStep(x, prefill=True)
+    step.run()
+    torch.cuda.synchronize()
+    parity.check_scores(cfg, x, step)
+    parity.check_selection(cfg, x, step)
+    parity.check_attention(cfg, x, step)
+    dec = MsaStep(x)
+    dec.run()
+    torch.cuda.synchronize()
+    assert torch.equal(dec.sel, step.sel)
+    err = (dec.out.float() - step.out.float()).abs()
+    lim = parity.OUT_ATOL + parity.OUT_RTOL * dec.out.float().abs()
+    assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
