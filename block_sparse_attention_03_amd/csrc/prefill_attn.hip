@@ -181,69 +181,94 @@ void bucket_count_kernel(const int32_t* __restrict__ sel, const int32_t* __restr
 // lists the nonempty buckets in order, those of more than small_cnt entries in
 // buckets and the others in small ([0] = how many, then their ids), so each
 // attention kernel launches only as many workgroups as there can be buckets
-// and none walks an empty one.
+// and none walks an empty one.  The counts go through in tiles of 8192: each
+// thread takes 8 consecutive buckets (two 16-byte loads), wavefront prefix
+// sums by lane shuffles, one LDS exchange of the 16 wavefront totals, and a
+// running carry from tile to tile.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u = __shfl_up(v, off, kWave);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(1024)
 void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                  int32_t* __restrict__ buckets, int32_t* __restrict__ small, int n,
                  int small_cnt) {
-    __shared__ int part[1024];
-    __shared__ int partl[1024];
-    __shared__ int parts[1024];
+    constexpr int kPer = 8;
+    constexpr int kScanWaves = 1024 / kWave;
+    __shared__ int wsum[3][kScanWaves];
+    __shared__ int carry[3];
     const int tid = threadIdx.x;
-    const int per = ceil_div(n, 1024);
-    const int a = min(n, tid * per), e = min(n, a + per);
-    // counts are read eight at a time, so that a thread's chunk costs one
-    // memory round trip per eight buckets rather than one per bucket
-    constexpr int kBatch = 8;
-    int sum = 0, nl = 0, ns = 0;
-    for (int i0 = a; i0 < e; i0 += kBatch) {
-        int c[kBatch];
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    if (tid < 3) carry[tid] = 0;
+    for (int t0 = 0; t0 < n; t0 += 1024 * kPer) {
+        const int a = t0 + tid * kPer;
+        int c[kPer];
+        if (a + kPer <= n) {  // counts is 256-byte aligned and a is a multiple of 8
+            const u32x4 v0 = *reinterpret_cast<const u32x4*>(counts + a);
+            const u32x4 v1 = *reinterpret_cast<const u32x4*>(counts + a + 4);
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) c[u] = (i0 + u < e) ? counts[i0 + u] : 0;
+            for (int u = 0; u < 4; ++u) {
+                c[u] = (int)v0[u];
+                c[4 + u] = (int)v1[u];
+            }
+        } else {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+            for (int u = 0; u < kPer; ++u) c[u] = (a + u < n) ? counts[a + u] : 0;
+        }
+        int sum = 0, nl = 0, ns = 0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
             sum += c[u];
             nl += c[u] > small_cnt;
             ns += c[u] > 0 && c[u] <= small_cnt;
         }
-    }
-    part[tid] = sum;
-    partl[tid] = nl;
-    parts[tid] = ns;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = (tid >= off) ? part[tid - off] : 0;
-        const int vl = (tid >= off) ? partl[tid - off] : 0;
-        const int vs = (tid >= off) ? parts[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        partl[tid] += vl;
-        parts[tid] += vs;
-        __syncthreads();
-    }
-    int run = part[tid] - sum;   // exclusive prefixes of this thread's chunk
-    int runl = partl[tid] - nl;
-    int runs = parts[tid] - ns;
-    for (int i0 = a; i0 < e; i0 += kBatch) {
-        int c[kBatch];
+        const int isum = wave_inclusive_sum(sum);
+        const int inl = wave_inclusive_sum(nl);
+        const int ins = wave_inclusive_sum(ns);
+        if (lane == kWave - 1) {
+            wsum[0][wave] = isum;
+            wsum[1][wave] = inl;
+            wsum[2][wave] = ins;
+        }
+        __syncthreads();  // wavefront totals and the carry are visible
+        int run = carry[0] + isum - sum;  // exclusive prefixes of this thread's buckets
+        int runl = carry[1] + inl - nl;
+        int runs = carry[2] + ins - ns;
+        for (int k = 0; k < wave; ++k) {
+            run += wsum[0][k];
+            runl += wsum[1][k];
+            runs += wsum[2][k];
+        }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) c[u] = (i0 + u < e) ? counts[i0 + u] : 0;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (i0 + u < e) {
-                offsets[i0 + u] = run;
+        for (int u = 0; u < kPer; ++u) {
+            if (a + u < n) {
+                offsets[a + u] = run;
                 run += c[u];
                 if (c[u] > small_cnt)
-                    buckets[1 + runl++] = i0 + u;
+                    buckets[1 + runl++] = a + u;
                 else if (c[u] > 0)
-                    small[1 + runs++] = i0 + u;
+                    small[1 + runs++] = a + u;
             }
         }
+        __syncthreads();  // every thread has read wsum and carry
+        if (tid == 1023) {  // the last thread ends at the running totals
+            carry[0] = run;
+            carry[1] = runl;
+            carry[2] = runs;
+        }
     }
-    if (tid == 1023) {
-        offsets[n] = part[1023];
-        buckets[0] = partl[1023];
-        small[0] = parts[1023];
+    __syncthreads();
+    if (tid == 0) {
+        offsets[n] = carry[0];
+        buckets[0] = carry[1];
+        small[0] = carry[2];
     }
 }
 
@@ -737,14 +762,19 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                        w.counts, NB);
     hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
-    const int G = s.Hq / s.Hkv;
+    // buckets of at most small_cnt entries (kSmallRows rows) are small
+    const int small_cnt = kSmallRows / (s.Hq / s.Hkv);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, w.buckets,
-                       w.small, NB, kSmallRows / G);
+                       w.small, NB, small_cnt);
     hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
                        w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
-    // at most one nonempty bucket per selection
-    const int n_bk = (int)std::min<int64_t>(NB, (int64_t)total_q * s.Hkv * kTopK);
-    hipLaunchKernelGGL(block_major_kernel, dim3(n_bk), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
+    // at most one nonempty bucket per selection, and at most one bucket of
+    // more than small_cnt entries per small_cnt + 1 selections
+    const int64_t n_sel = (int64_t)total_q * s.Hkv * kTopK;
+    const int n_bk = (int)std::min<int64_t>(NB, n_sel);
+    const int n_large = (int)std::min<int64_t>(NB, n_sel / (small_cnt + 1));
+    if (n_large > 0)
+        hipLaunchKernelGGL(block_major_kernel, dim3(n_large), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
                        block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
     hipLaunchKernelGGL(bucket_small_kernel, dim3(n_bk), dim3(kDecThreads), 0, st, q, k_cache,
