@@ -414,7 +414,7 @@ def main():
     if not args.no_also:
         also = {}
 
-        def decode_line(c, n_layers, n_steps):
+        def decode_line(c, n_layers, n_steps, graph=False):
             ls = make_layers(c, n_layers)
             f = [MsaStep(x, fused=True) for x in ls]
             fo = [MsaStep(x) for x in ls]
@@ -425,13 +425,15 @@ def main():
                     "layer_step_hbm_frac": round(b_ / (ms_ * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
                     "algorithmic_bytes": int(b_),
                     "us_four_calls": round(ms4_ * 1e3, 2), "layers": n_layers}
+            if graph:  # launch-bound: the same steps replayed as one HIP graph per pass
+                line["us_hip_graph"] = round(time_graph(f, 4 * n_layers, 2 * n_layers) * 1e3, 2)
             del f, fo, ls
             torch.cuda.empty_cache()
             return line
 
         # decode at 4096 tokens, batch 1 (2.6 MB: launch-bound)
         c1 = gen.config(1)
-        also[c1.name] = decode_line(c1, 128, max(128, args.steps))
+        also[c1.name] = decode_line(c1, 128, max(128, args.steps), graph=True)
         # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
         c5 = gen.config(5)
         also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4))
