@@ -18,8 +18,9 @@ each other with no host or timing gaps.  One pair of HIP events on the
 kernels' stream brackets the K steps; ``value`` is their mean.  The roofline
 kernel is timed the same way: K back-to-back calls of it over the layers.
 
-Also reported (``also``): decode at 4096 tokens (batch 1), ragged decode (16
-sequences, 4096 to 524,288 tokens), 1M-context decode (batch 4) with its
+Also reported (``also``): decode at 4096 tokens (batch 1), the 60k decode with
+one index key per KV group (H_idx = H_kv), ragged decode (16 sequences, 4096 to
+524,288 tokens), 1M-context decode (batch 4) with its
 scoring pass measured separately, 8192-token chunked prefill onto a
 57,344-token prefix (tokens/s), multi-query decode (4 drafts per sequence),
 the selection kernel against torch.topk, the dense GQA decode baseline
@@ -434,6 +435,9 @@ def main():
         # decode at 4096 tokens, batch 1 (2.6 MB: launch-bound)
         c1 = gen.config(1)
         also[c1.name] = decode_line(c1, 128, max(128, args.steps), graph=True)
+        # the 60k decode with one index key per KV group (H_idx = H_kv): 558 MB
+        cg = gen.config(2).with_idx_heads(gen.config(2).num_kv_heads)
+        also["paged_decode_b8_ctx60k_per_group_index_keys"] = decode_line(cg, 4, max(40, args.steps // 4))
         # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
         c5 = gen.config(5)
         also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4))

@@ -35,6 +35,10 @@ namespace {
 
 constexpr int kScoreWaves = 4;  // blocks per workgroup (one per wavefront)
 
+// kInvisible: write -inf for the blocks past every row's position (the ABI's
+// score rows); the fused decode step, whose selection never reads them,
+// skips those stores.
+template <bool kInvisible>
 __global__ __launch_bounds__(kScoreWaves * kWave)
 void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
                         const uint16_t* __restrict__ kidx,    // [P, Hidx, 128, 64]
@@ -70,6 +74,7 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     const int kg = lane / 16;    // lane group: reduction-index slice / result row quad
 
     if (!any_visible) {
+        if (!kInvisible) return;
         for (int r0 = 0; r0 < nrows; r0 += kWave) {
             const int rho = r0 + lane;
             if (rho < nrows) {
@@ -384,7 +389,7 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
         return hipGetLastError();
     }
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
-    hipLaunchKernelGGL(index_score_kernel, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
+    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
                        block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk);
     return hipGetLastError();
 }
@@ -394,9 +399,11 @@ hipError_t msa_launch_index_score_decode(const MsaShape& s, const uint16_t* q_id
                                          const int32_t* seq_lens, float* scores, hipStream_t st) {
     using namespace msa;
     if (s.B == 0) return hipSuccess;
+    // scores past each row's own block stay unwritten: the decode step's
+    // selection gives blocks past b_loc no key and never reads their values
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
-    hipLaunchKernelGGL(index_score_kernel, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
-                       block_table, seq_lens, static_cast<const int32_t*>(nullptr), scores, s.Hkv,
-                       s.Hidx, s.maxblk);
+    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(kScoreWaves * kWave), 0, st, q_idx,
+                       kidx, block_table, seq_lens, static_cast<const int32_t*>(nullptr), scores,
+                       s.Hkv, s.Hidx, s.maxblk);
     return hipGetLastError();
 }

@@ -174,7 +174,9 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t *dims, int32_t total_q, co
 /*
  * The whole decode layer-step in three launches (the fused form of the four
  * calls above; same results, bit for bit).  Scoring runs as in
- * msa_index_score; then every (row r = s*H_kv + g, page slot i) workgroup
+ * msa_index_score (into the workspace, leaving the scores of blocks past each
+ * row's own block unwritten, since the selection never reads them); then
+ * every (row r = s*H_kv + g, page slot i) workgroup
  * makes the row's top-k selection itself from the block scores -- the same
  * deterministic rule as msa_topk_blocks -- maps its i-th selected block to a
  * physical page through block_table (the row's page table, built on chip:
