@@ -272,6 +272,127 @@ void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offse
     }
 }
 
+// Small inverse map: the whole map (count, scan, bucket lists, placement)
+// in one 1024-thread workgroup with the bucket counts in LDS, for a few
+// queries per sequence (multi-query decode), where the four-kernel form is
+// dominated by launch latency.  Counts, then offsets, are 16-bit halves of
+// LDS words (at most kSmallMapSel selections); ranks within a bucket come
+// from the LDS atomics.  Only the nonempty buckets' counts and offsets are
+// written to the workspace: they are the only ones the attention kernels
+// read.
+constexpr int kSmallMapBuckets = 49152;
+constexpr int kSmallMapSel = 16384;
+
+__global__ __launch_bounds__(1024)
+void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
+                              PrefillWs w, int total_q, int B, int Hkv, int maxblk,
+                              int small_cnt) {
+    __shared__ uint32_t cnt2[kSmallMapBuckets / 2];  // two 16-bit counts (later offsets) per word
+    __shared__ uint16_t rank[kSmallMapSel];
+    __shared__ int seq_of[kSmallMapSel / kTopK];      // query token -> sequence
+    __shared__ int wsum[3][1024 / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int NB = B * Hkv * maxblk;
+    const int n_sel = total_q * Hkv * kTopK;
+    for (int i = tid; i < (NB + 1) / 2; i += 1024) cnt2[i] = 0u;
+    for (int sq = tid; sq < B; sq += 1024)
+        for (int t = cu_q[sq]; t < cu_q[sq + 1]; ++t) seq_of[t] = sq;
+    __syncthreads();
+
+    // count: each selection's rank in its bucket
+    auto bucket_of = [&](int e, int b) {
+        const int t = e / (Hkv * kTopK);
+        const int g = (e / kTopK) % Hkv;
+        return (seq_of[t] * Hkv + g) * maxblk + b;
+    };
+    for (int e = tid; e < n_sel; e += 1024) {
+        const int b = sel[e];
+        if (b >= 0 && b < maxblk) {
+            const int bk = bucket_of(e, b);
+            const int sh = 16 * (bk & 1);
+            const uint32_t old = atomicAdd(&cnt2[bk >> 1], 1u << sh);
+            rank[e] = (uint16_t)((old >> sh) & 0xFFFFu);
+        }
+    }
+    __syncthreads();
+
+    // scan: thread tid takes buckets [a, e); wavefront prefix sums, then the
+    // 16 wavefront totals through LDS
+    const int per = ceil_div(NB, 1024);
+    const int a = min(NB, tid * per), e_end = min(NB, a + per);
+    auto count_at = [&](int i) { return (int)((cnt2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
+    int sum = 0, nl = 0, ns = 0;
+    for (int i = a; i < e_end; ++i) {
+        const int c = count_at(i);
+        sum += c;
+        nl += c > small_cnt;
+        ns += c > 0 && c <= small_cnt;
+    }
+    int isum = sum, inl = nl, ins = ns;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int u0 = __shfl_up(isum, off, kWave), u1 = __shfl_up(inl, off, kWave),
+                  u2 = __shfl_up(ins, off, kWave);
+        if (lane >= off) {
+            isum += u0;
+            inl += u1;
+            ins += u2;
+        }
+    }
+    if (lane == kWave - 1) {
+        wsum[0][wave] = isum;
+        wsum[1][wave] = inl;
+        wsum[2][wave] = ins;
+    }
+    __syncthreads();
+    int run = isum - sum, runl = inl - nl, runs = ins - ns;
+    for (int k = 0; k < wave; ++k) {
+        run += wsum[0][k];
+        runl += wsum[1][k];
+        runs += wsum[2][k];
+    }
+    for (int i = a; i < e_end; ++i) {
+        const int c = count_at(i);
+        if (c > 0) {
+            w.counts[i] = c;
+            w.offsets[i] = run;
+            if (c > small_cnt)
+                w.buckets[1 + runl++] = i;
+            else
+                w.small[1 + runs++] = i;
+        }
+        run += c;
+    }
+    if (tid == 1023) {
+        w.buckets[0] = runl;
+        w.small[0] = runs;
+    }
+    __syncthreads();  // every count has been read
+    // counts -> exclusive offsets in place (each thread its own buckets)
+    run = isum - sum;
+    for (int k = 0; k < wave; ++k) run += wsum[0][k];
+    for (int i = a; i < e_end; ++i) {
+        const int c = count_at(i);
+        atomicAnd(&cnt2[i >> 1], ~(0xFFFFu << (16 * (i & 1))));
+        atomicOr(&cnt2[i >> 1], (uint32_t)run << (16 * (i & 1)));
+        run += c;
+    }
+    __syncthreads();
+
+    // place: entries[offset + rank] = query << 4 | slot
+    for (int e = tid; e < n_sel; e += 1024) {
+        const int b = sel[e];
+        if (b >= 0 && b < maxblk) {
+            const int bk = bucket_of(e, b);
+            const int off = count_at(bk);
+            const int t = e / (Hkv * kTopK);
+            w.entries[off + rank[e]] = (t << 4) | (e % kTopK);
+        }
+    }
+}
+
 // Pass 3: the tile places each selection at offsets[bucket] + its tile's base
 // in the bucket + its rank among the tile's selections of that block (LDS
 // counters; entries within a bucket are in no particular order).
@@ -758,16 +879,21 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     PrefillWs w = prefill_ws(ws, s.B, s.Hkv, s.maxblk, total_q, s.Hq);
     const int tiles = max_tiles(total_q, s.B, s.Hkv);
     const size_t map_lds = (size_t)s.maxblk * sizeof(int32_t);
-    hipLaunchKernelGGL(zero_kernel, dim3(min(1024, ceil_div(NB, 256))), dim3(256), 0, st,
-                       w.counts, NB);
-    hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
-                       w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
     // buckets of at most small_cnt entries (kSmallRows rows) are small
     const int small_cnt = kSmallRows / (s.Hq / s.Hkv);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets, w.buckets,
-                       w.small, NB, small_cnt);
-    hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel, cu_q,
-                       w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
+    if (NB <= kSmallMapBuckets && (int64_t)total_q * s.Hkv * kTopK <= kSmallMapSel) {
+        hipLaunchKernelGGL(inverse_map_small_kernel, dim3(1), dim3(1024), 0, st, sel, cu_q, w,
+                           total_q, s.B, s.Hkv, s.maxblk, small_cnt);
+    } else {
+        hipLaunchKernelGGL(zero_kernel, dim3(min(1024, ceil_div(NB, 256))), dim3(256), 0, st,
+                           w.counts, NB);
+        hipLaunchKernelGGL(bucket_count_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel,
+                           cu_q, w.counts, w.tile_base, s.B, s.Hkv, s.maxblk);
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets,
+                           w.buckets, w.small, NB, small_cnt);
+        hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel,
+                           cu_q, w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
+    }
     // at most one nonempty bucket per selection, and at most one bucket of
     // more than small_cnt entries per small_cnt + 1 selections
     const int64_t n_sel = (int64_t)total_q * s.Hkv * kTopK;
