@@ -64,6 +64,8 @@ struct PrefillWs {
     int32_t* entries;    // [total_q * Hkv * k]: query << 4 | slot, grouped by bucket
     uint16_t* part_o;    // [total_q, Hq, k, 128] bf16
     float* part_lse;     // [total_q, Hq, k]
+    uint16_t* trash_o;   // [128] bf16: where padding rows' partial stores go
+    float* trash_lse;    // [64]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -88,12 +90,16 @@ __host__ __device__ inline PrefillWs prefill_ws(void* base, int B, int Hkv, int 
     w.part_o = reinterpret_cast<uint16_t*>(p);
     p += align256((size_t)total_q * Hq * kTopK * kHeadDim * 2);
     w.part_lse = reinterpret_cast<float*>(p);
+    p += align256((size_t)total_q * Hq * kTopK * 4);
+    w.trash_o = reinterpret_cast<uint16_t*>(p);
+    p += align256(kHeadDim * 2);
+    w.trash_lse = reinterpret_cast<float*>(p);
     return w;
 }
 
 __host__ __device__ inline size_t prefill_ws_size(int B, int Hkv, int maxblk, int total_q, int Hq) {
     PrefillWs w = prefill_ws(nullptr, B, Hkv, maxblk, total_q, Hq);
-    return reinterpret_cast<size_t>(w.part_lse) + align256((size_t)total_q * Hq * kTopK * 4);
+    return reinterpret_cast<size_t>(w.trash_lse) + align256(kWave * 4);
 }
 
 __global__ void zero_kernel(int32_t* a, int na) {
@@ -483,10 +489,13 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 
     // Row n of a tile: its query, head and selection slot.  Rows past the
     // bucket repeat its last row (real data; results discarded).
-    auto row_info = [&](int tile, int* t_out, int* head_out, int* slot_out) {
+    // Row n of a tile: its (query << 4 | slot) entry -- fetched two tiles
+    // ahead -- and from it the query, head and slot.  Rows past the bucket
+    // repeat its last row (real data; results discarded).
+    auto entry_of = [&](int tile) { return w.entries[base + min(tile * 32 + n, nrows - 1) / G]; };
+    auto row_info = [&](int tile, int entry, int* t_out, int* head_out, int* slot_out) {
         const int rho0 = tile * 32 + n;
         const int rho = rho0 < nrows ? rho0 : nrows - 1;
-        const int entry = w.entries[base + rho / G];
         *t_out = entry >> 4;
         *slot_out = entry & 15;
         *head_out = g * G + rho % G;
@@ -504,14 +513,23 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         }
     };
 
+    // Every iteration issues the same memory operations -- the next tile's
+    // query rows and the entries two tiles ahead, clamped to the bucket's
+    // last row past its end, and partial stores that padding rows send to a
+    // trash row -- so that each wait covers exactly the loads it needs and
+    // never the previous tile's stores.
     int tile = wave;
+    if (tile * 32 >= nrows) return;  // wavefront-uniform; no workgroup barrier follows
     int t = 0, head = 0, slot = 0;
-    bool row_ok = false;
+    bool row_ok = row_info(tile, entry_of(tile), &t, &head, &slot);
+    int entry_next = entry_of(tile + kWaves);
     u32x4 qraw[8];
-    if (tile * 32 < nrows) {
-        row_ok = row_info(tile, &t, &head, &slot);
-        gather_q(t, head, qraw);
-    }
+    gather_q(t, head, qraw);
+    // wait for the first tile's loads here, so that at the loop head neither
+    // path has its query rows in flight and no wait there reaches the
+    // previous tile's stores (s_waitcnt immediate: vmcnt 0, other counters
+    // unconstrained)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     for (; tile * 32 < nrows; tile += kWaves) {
         // Q rows -> staging tile -> B operands (k-step i of lane half h: dims 64h + 8i .. +7)
@@ -527,10 +545,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         const bool cur_ok = row_ok;
         // next tile's rows are gathered while this one computes
         const int next = tile + kWaves;
-        if (next * 32 < nrows) {
-            row_ok = row_info(next, &t, &head, &slot);
-            gather_q(t, head, qraw);
-        }
+        row_ok = row_info(next, entry_next, &t, &head, &slot);
+        gather_q(t, head, qraw);
+        entry_next = entry_of(next + kWaves);
 
         // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
         // token 32mt + 8(v/4) + 4h + v%4 of row n.  Operands of token tile
@@ -645,10 +662,12 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
             const int r = lane / 16 + 4 * it;
             const int o = __shfl(orow, r, kWave);
             const u32x4 v = *reinterpret_cast<const u32x4*>(tbuf + r * kKStride + 8 * (lane % 16));
-            if (o >= 0) *reinterpret_cast<u32x4*>(w.part_o + (size_t)o * kHeadDim + 8 * (lane % 16)) = v;
+            uint16_t* dst = (o >= 0) ? w.part_o + (size_t)o * kHeadDim : w.trash_o;
+            *reinterpret_cast<u32x4*>(dst + 8 * (lane % 16)) = v;
         }
-        if (cur_ok && h == 0)
-            w.part_lse[((size_t)cur_t * Hq + cur_head) * kTopK + cur_slot] = mx * scale_log2 * kLn2 + __logf(sum);
+        float* ldst = (cur_ok && h == 0) ? w.part_lse + ((size_t)cur_t * Hq + cur_head) * kTopK + cur_slot
+                                         : w.trash_lse + lane;
+        *ldst = mx * scale_log2 * kLn2 + __logf(sum);
         __builtin_amdgcn_wave_barrier();
     }
 }
