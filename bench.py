@@ -57,6 +57,8 @@ def parse():
                     help="only run plain 256 MiB device copies (PMC byte-counter calibration)")
     ap.add_argument("--score-only", action="store_true",
                     help="only run the headline's index_score_kernel calls (PMC passes)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run chunked-prefill layer-steps, 8192 tokens on 57,344 (PMC passes)")
     return ap.parse_args()
 
 
@@ -341,6 +343,12 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": a.numel() * 4, "launches": 4}))
+        return
+    if args.prefill_only:
+        cfg = gen.config(3)
+        st3 = [MsaStep(x) for x in make_layers(cfg, 2)]
+        ms = time_calls([s_.run for s_ in st3], args.steps, args.warmup)
+        print(json.dumps({"prefill_step_ms": ms, "launches": args.steps + args.warmup}))
         return
     if args.score_only:
         cfg = gen.config(2)
