@@ -205,14 +205,11 @@ void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
     __shared__ __attribute__((aligned(16))) DecodeShared sh;
     __shared__ int32_t sel_idx[kTopK];
     __shared__ int32_t sel_page[kTopK];
-    // gridDim.x = kTopK / slots-per-workgroup: workgroup x attends slots
-    // x, x + gridDim.x, ... (more than one when the rows would not all fit on
-    // the chip at once, so that each row's selection is made once per
-    // resident workgroup rather than once per round)
     // the selection's LDS lives in the V tile, which is written only after
     // the barrier that ends the selection
     static_assert(sizeof(SelectShared<W>) <= sizeof(sh.vs), "selection scratch");
     SelectShared<W>* ssh = reinterpret_cast<SelectShared<W>*>(sh.vs);
+    const int slot = blockIdx.x;
     const int r = blockIdx.y;
     const int s = r / Hkv;
     const int g = r % Hkv;
@@ -237,20 +234,18 @@ void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
             sel_page[pos] = pg;
         });
     __syncthreads();
-    if (blockIdx.x == 0) {
+    if (slot >= n_sel) return;  // uniform
+    const int b = sel_idx[slot];
+    if (slot == 0) {
         if (threadIdx.x < kTopK && sel_out) sel_out[(size_t)r * kTopK + threadIdx.x] = sel_idx[threadIdx.x];
         if (threadIdx.x == 0) row_lens[r] = (n_sel - 1) * kBlock + (p - kBlock * b_loc + 1);
     }
-    for (int slot = blockIdx.x; slot < n_sel; slot += gridDim.x) {  // uniform
-        if (slot != (int)blockIdx.x) __syncthreads();  // the previous page's LDS reads are done
-        const int b = sel_idx[slot];
-        // ascending order puts the own (partial) block last
-        const int nv = (slot == n_sel - 1) ? p - kBlock * b_loc + 1 : kBlock;
-        const int pg = PAGES ? sel_page[slot] : block_table[(size_t)s * maxblk + b];
-        const size_t page_off = ((size_t)pg * Hkv + g) * kBlock * kHeadDim;
-        attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, Hq / Hkv, Hq, r, slot, ws,
-                    R, scale_log2, sh);
-    }
+    // ascending order puts the own (partial) block last
+    const int nv = (slot == n_sel - 1) ? p - kBlock * b_loc + 1 : kBlock;
+    const int pg = PAGES ? sel_page[slot] : block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)pg * Hkv + g) * kBlock * kHeadDim;
+    attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, Hq / Hkv, Hq, r, slot, ws, R,
+                scale_log2, sh);
 }
 
 // One thread per (row, head, dim): Log-Sum-Exp merge of the row's pages.
@@ -345,11 +340,7 @@ static hipError_t launch_fused(const MsaShape& s, const float* scores, const int
                                void* ws, hipStream_t st) {
     using namespace msa;
     const int R = s.B * s.Hkv;
-    // slots per workgroup: the fewest (a power of two) that let every page
-    // workgroup be resident at once (four per CU on 256 CUs)
-    int spw = 1;
-    while (spw < kTopK && (int64_t)R * kTopK / spw > 4 * 256) spw *= 2;
-    hipLaunchKernelGGL((decode_fused_kernel<NPT, W, PAGES>), dim3(kTopK / spw, R), dim3(kDecThreads), 0, st,
+    hipLaunchKernelGGL((decode_fused_kernel<NPT, W, PAGES>), dim3(kTopK, R), dim3(kDecThreads), 0, st,
                        scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws,
                        s.Hq, s.Hkv, R, s.maxblk, s.scale * kLog2e);
     return hipGetLastError();
