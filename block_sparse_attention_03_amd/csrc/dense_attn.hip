@@ -418,13 +418,14 @@ void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         // the row's own block is visible)
         const int lim = p - b * kBlock;
         if (__ballot(lim < kBlock - 1)) {
+            // the lane's token is 32mt + 8(v/4) + 4h + v%4: compare the
+            // constant part against lim - 4h (no per-lane index registers)
+            const int limh = lim - 4 * h;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int tk = 32 * mt + 8 * (v / 4) + 4 * h + (v % 4);
-                    if (tk > lim) sacc[mt][v] = -__builtin_inff();
-                }
+                for (int v = 0; v < 16; ++v)
+                    if (32 * mt + 8 * (v / 4) + (v % 4) > limh) sacc[mt][v] = -__builtin_inff();
         }
         float mx = -__builtin_inff();
 #pragma unroll

@@ -503,14 +503,12 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     };
     // Coalesced gather of a tile's 32 query rows: instruction it moves rows
     // 4it .. 4it+3, 16 lanes x 16 bytes each.
+    // Direct gather of a tile's query rows into B operands: lane (n, h) loads
+    // dims 64h + 8i .. +7 of its row n for k-step i.
     auto gather_q = [&](int t_n, int head_n, u32x4* raw) {
-        const int qrow = t_n * Hq + head_n;  // row n's q row (< 2^27)
+        const uint16_t* qrow = q + ((size_t)t_n * Hq + head_n) * kHeadDim + 64 * h;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = lane / 16 + 4 * it;
-            const size_t off = (size_t)__shfl(qrow, r, kWave) * kHeadDim;
-            raw[it] = ld16(q + off + 8 * (lane % 16));
-        }
+        for (int i = 0; i < 8; ++i) raw[i] = ld16(qrow + 8 * i);
     };
 
     // Every iteration issues the same memory operations -- the next tile's
@@ -532,15 +530,10 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
     for (; tile * 32 < nrows; tile += kWaves) {
-        // Q rows -> staging tile -> B operands (k-step i of lane half h: dims 64h + 8i .. +7)
-#pragma unroll
-        for (int it = 0; it < 8; ++it)
-            *reinterpret_cast<u32x4*>(tbuf + (lane / 16 + 4 * it) * kKStride + 8 * (lane % 16)) = qraw[it];
-        __builtin_amdgcn_wave_barrier();
+        // B operands (k-step i of lane half h: dims 64h + 8i .. +7)
         bf16x8 qb[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            qb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(tbuf + n * kKStride + 64 * h + 8 * i));
+        for (int i = 0; i < 8; ++i) qb[i] = as_bf16x8(qraw[i]);
         const int cur_t = t, cur_slot = slot, cur_head = head;
         const bool cur_ok = row_ok;
         // next tile's rows are gathered while this one computes
@@ -576,13 +569,14 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         // causal cut inside the query's own block
         const int lim = pos0 + cur_t - tok0;  // token index (within block) must be <= lim
         if (__ballot(lim < kBlock - 1)) {  // only tiles holding a row of this block's own queries
+            // the lane's token is 32mt + 8(v/4) + 4h + v%4: compare the
+            // constant part against lim - 4h (no per-lane index registers)
+            const int limh = lim - 4 * h;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int tk = 32 * mt + 8 * (v / 4) + 4 * h + (v % 4);
-                    if (tk > lim) sacc[mt][v] = -__builtin_inff();
-                }
+                for (int v = 0; v < 16; ++v)
+                    if (32 * mt + 8 * (v / 4) + (v % 4) > limh) sacc[mt][v] = -__builtin_inff();
         }
         float mx = -__builtin_inff();
 #pragma unroll
