@@ -38,6 +38,10 @@ SMALL = [
     # scored by the per-block kernel and attended KV-block-major
     gen.MsaConfig("multi_query_decode", [9000, 20000, 3000, 700], [4, 4, 2, 3], 12, 3,
                   permute_pages=True, seed=48),
+    # whole sequences new (positions from 0: early queries see fewer than k
+    # blocks), G = 1 (buckets of up to 32 queries are small)
+    gen.MsaConfig("prefill_from_scratch_g1", [1500, 300, 2600], [1500, 300, 2600], 4, 4,
+                  permute_pages=True, seed=59),
 ]
 
 
