@@ -28,6 +28,7 @@ EXPORTED = (
     "msa_sparse_attn_prefill", "msa_decode_workspace_size", "msa_prefill_workspace_size",
     "msa_status_string", "msa_abi_version", "msa_decode_step", "msa_decode_step_workspace_size",
     "msa_dense_attn_decode", "msa_dense_decode_workspace_size", "msa_dense_attn_prefill",
+    "msa_validate_inputs",
 )
 
 
@@ -76,11 +77,12 @@ def lib():
         L.msa_decode_step_workspace_size.restype = SZ
         L.msa_dense_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
         L.msa_dense_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P]
+        L.msa_validate_inputs.argtypes = [D, I32, P, P, P, P, P]
         L.msa_dense_decode_workspace_size.argtypes = [D]
         L.msa_dense_decode_workspace_size.restype = SZ
         for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
                   "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_decode_step",
-                  "msa_dense_attn_decode", "msa_dense_attn_prefill"):
+                  "msa_dense_attn_decode", "msa_dense_attn_prefill", "msa_validate_inputs"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_decode_workspace_size.argtypes = [D]
         L.msa_decode_workspace_size.restype = SZ
@@ -279,3 +281,19 @@ def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_
             _ptr(lse, F32, "lse", (total_q, Hq)) if lse is not None else None)
     _check(lib().msa_dense_attn_prefill(ctypes.byref(d), total_q, *args, _stream(stream)),
            "msa_dense_attn_prefill")
+
+
+MSA_FAULT_SEQ_LEN, MSA_FAULT_CU_Q, MSA_FAULT_BLOCK_TABLE = 1, 2, 4
+
+
+def msa_validate_inputs(dims, total_q, block_table, seq_lens, cu_q, status, stream=None):
+    """Device-side check of the content preconditions; `status` (one int32 on
+    the device) receives 0 or the OR of the MSA_FAULT_* bits found."""
+    d = dims
+    B = d.num_seqs
+    args = (_ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)),
+            _ptr(cu_q, I32, "cu_q", (B + 1,)) if cu_q is not None else None,
+            _ptr(status, I32, "status", (1,)))
+    _check(lib().msa_validate_inputs(ctypes.byref(d), total_q, *args, _stream(stream)),
+           "msa_validate_inputs")

@@ -233,6 +233,21 @@ msa_status_t msa_dense_attn_prefill(const msa_dims_t* dims, int32_t total_q, con
                                              cu_q, out, lse, static_cast<hipStream_t>(stream)));
 }
 
+msa_status_t msa_validate_inputs(const msa_dims_t* dims, int32_t total_q, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* cu_q, int32_t* status,
+                                 void* stream) {
+    MsaShape s;
+    msa_status_t st = check_dims(dims, &s);
+    if (st != MSA_SUCCESS) return st;
+    if (cu_q && (st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (!block_table || !seq_lens || !status) return MSA_ERROR_INVALID_VALUE;
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (cu_q && !aligned(cu_q, 4)) ||
+        !aligned(status, 4))
+        return MSA_ERROR_INVALID_VALUE;
+    return launched(msa_launch_validate(s, cu_q ? total_q : s.B, block_table, seq_lens, cu_q, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 const char* msa_status_string(msa_status_t status) {
     switch (status) {
         case MSA_SUCCESS: return "MSA_SUCCESS";

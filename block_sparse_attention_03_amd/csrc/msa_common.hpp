@@ -126,6 +126,9 @@ struct MsaShape {
     float scale;  // resolved softmax scale (> 0)
 };
 
+hipError_t msa_launch_validate(const MsaShape& s, int total_q, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* cu_q, int32_t* status,
+                               hipStream_t st);
 hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t* q_idx,
                                   const uint16_t* kidx, const int32_t* block_table,
                                   const int32_t* seq_lens, const int32_t* cu_q, float* scores,

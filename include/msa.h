@@ -228,6 +228,26 @@ msa_status_t msa_dense_attn_prefill(const msa_dims_t *dims, int32_t total_q, con
                                     const int32_t *block_table, const int32_t *seq_lens,
                                     const int32_t *cu_q, uint16_t *out, float *lse, void *stream);
 
+/*
+ * Device-side check of the content preconditions listed at the top of this
+ * file, for callers that want them verified (not a hot-path call): for every
+ * sequence s, 1 <= seq_lens[s] <= max_blocks_per_seq*Bk; with cu_q,
+ * cu_q[0] = 0, cu_q[B] = total_q and 0 <= cu_q[s+1]-cu_q[s] <= seq_lens[s];
+ * block_table[s][b] in [0, num_pages) for b < ceil(seq_lens[s]/Bk).
+ *   cu_q   [B+1] or NULL (decode: one query per sequence; total_q ignored)
+ *   status one int32 in device memory (output): 0, or the OR of the
+ *          msa_input_fault_t bits found, written on `stream`.
+ * It reads only within the arrays' declared sizes, whatever their content.
+ */
+typedef enum {
+    MSA_FAULT_SEQ_LEN = 1,     /* a sequence length below 1 or past the block table */
+    MSA_FAULT_CU_Q = 2,        /* query ranges not within [0, total_q] or longer than L */
+    MSA_FAULT_BLOCK_TABLE = 4  /* a used block-table entry outside [0, num_pages) */
+} msa_input_fault_t;
+msa_status_t msa_validate_inputs(const msa_dims_t *dims, int32_t total_q,
+                                 const int32_t *block_table, const int32_t *seq_lens,
+                                 const int32_t *cu_q, int32_t *status, void *stream);
+
 /* Workspace sizes in bytes (0 for invalid dims). */
 size_t msa_decode_workspace_size(const msa_dims_t *dims);
 size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);

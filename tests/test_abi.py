@@ -159,3 +159,14 @@ def test_calibration_library_exports():
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     # argument errors are caught before any launch
     assert c.msa_calib_read_grid(None, 16, 4, None, 0, None) != 0
+
+
+def test_validate_inputs_errors():
+    lib = L.lib()
+    d = dims()
+    assert lib.msa_validate_inputs(ctypes.byref(d), 5, None, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_validate_inputs(ctypes.byref(d), 5, A, A, A, None, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_validate_inputs(ctypes.byref(d), 5, A, A, A, MIS, None) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_validate_inputs(ctypes.byref(d), -1, A, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
+    bad = dims(topk=8)
+    assert lib.msa_validate_inputs(ctypes.byref(bad), 5, A, A, A, A, None) == L.MSA_ERROR_NOT_SUPPORTED

@@ -488,3 +488,37 @@ def test_prefill_entry_with_one_query_per_sequence():
     err = (dec.out.float() - step.out.float()).abs()
     lim = parity.OUT_ATOL + parity.OUT_RTOL * dec.out.float().abs()
     assert bool((err <= lim).all()), f"max abs diff {err.max().item():.3g}"
+
+
+def test_validate_inputs_finds_each_fault():
+    """msa_validate_inputs: 0 on the generated inputs, and the right bit for a
+    length of 0, a length past the block table, a decreasing query range and
+    a page index past the pool."""
+    cfg = gen.MsaConfig("validate", [3000, 700, 5000], [3, 1, 2], 8, 2, permute_pages=True, seed=60)
+    x = gen.make_inputs(cfg, device="cuda")
+    d = L.dims_for(cfg)
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+
+    def run(bt, sl, cq):
+        L.msa_validate_inputs(d, cfg.total_q, bt, sl, cq, status)
+        torch.cuda.synchronize()
+        return int(status.item())
+
+    assert run(x.block_table, x.seq_lens, x.cu_q) == 0
+    assert run(x.block_table, x.seq_lens, None) == 0  # decode-style check, no query ranges
+    sl = x.seq_lens.clone()
+    sl[1] = 0
+    assert run(x.block_table, sl, x.cu_q) & L.MSA_FAULT_SEQ_LEN
+    sl = x.seq_lens.clone()
+    sl[0] = cfg.max_blocks * cfg.block_size + 1
+    assert run(x.block_table, sl, x.cu_q) == L.MSA_FAULT_SEQ_LEN
+    cq = x.cu_q.clone()
+    cq[2] = cq[1] - 1
+    assert run(x.block_table, x.seq_lens, cq) == L.MSA_FAULT_CU_Q
+    bt = x.block_table.clone()
+    bt[2, 3] = cfg.num_pages
+    assert run(bt, x.seq_lens, x.cu_q) == L.MSA_FAULT_BLOCK_TABLE
+    bt[0, 0] = -1
+    sl = x.seq_lens.clone()
+    sl[1] = 0
+    assert run(bt, sl, x.cu_q) == L.MSA_FAULT_BLOCK_TABLE | L.MSA_FAULT_SEQ_LEN | L.MSA_FAULT_CU_Q
