@@ -87,14 +87,35 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     }
 
     // A operands: the block's index keys.  Tile mt covers tokens 16*mt..16*mt+15;
-    // k-step i of lane group kg takes dims 32*i + 8*kg .. +7 of the token row.
-    const uint16_t* kb = kidx + ((size_t)page * Hidx + ih) * kBlock * kIdxDim;
+    // k-step i of lane group kg takes dims 32*i + 8*kg .. +7 (16-byte chunk
+    // 4i + kg) of the token row.  The 16 KB arrive in sixteen contiguous 1 KB
+    // loads (load j: tokens 8j .. 8j+7; lane l: token 8j + l/8, chunk l % 8)
+    // -- whole 128-byte lines per instruction, where loading in operand order
+    // would request half lines -- and reach operand order through this
+    // wavefront's 8 KB LDS tile, half a block at a time.  Chunk c of local
+    // token t sits at chunk c ^ (t mod 8), so the operand reads of 8
+    // consecutive tokens fall in 8 different bank groups.  LDS operations of
+    // one wavefront complete in order, so the tile needs no barrier.
+    __shared__ __attribute__((aligned(16))) u32x4 kstage[kScoreWaves][kBlock / 2 * 8];
+    u32x4* st = kstage[wave];
+    const u32x4* kb = reinterpret_cast<const u32x4*>(kidx + ((size_t)page * Hidx + ih) * kBlock * kIdxDim);
+    u32x4 raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j] = ld16_stream(kb + kWave * j + lane);
     bf16x8 a[8][2];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        const uint16_t* row = kb + (mt * 16 + m_in) * kIdxDim;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[mt][i] = as_bf16x8(ld16_stream(row + 32 * i + 8 * kg));
+        for (int jj = 0; jj < 8; ++jj) {
+            const int t = 8 * jj + lane / 8;  // local token (tokens 64 half + t)
+            st[t * 8 + ((lane % 8) ^ (t & 7))] = raw[8 * half + jj];
+        }
+#pragma unroll
+        for (int mq = 0; mq < 4; ++mq) {
+            const int t = 16 * mq + m_in;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[4 * half + mq][i] = as_bf16x8(st[t * 8 + ((4 * i + kg) ^ (t & 7))]);
+        }
     }
 
     const int tok0 = b * kBlock;
