@@ -64,40 +64,19 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
             const int tok = tid / 16 + 16 * it;
             vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
         }
-        // K of this wave's 32 tokens as eight contiguous 1 KB loads (load j:
-        // tokens 32w + 4j .. +3; lane l: token 32w + 4j + l/16, chunk l % 16)
-        // -- whole lines per instruction, where loading in operand order
-        // would request quarter lines
+        // K of this wave's 32 tokens: contiguous loads, then operand order
+        // through the V tile, which is written only after every wave has read
+        // its K (barrier)
         u32x4 kraw[8];
-        const u32x4* kp4 = reinterpret_cast<const u32x4*>(kp) + 32 * wave * (kHeadDim / 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kraw[j] = ld16_stream(kp4 + kWave * j + lane);
+        load_k_rows(kp, wave, lane, kraw);
         // Q operands: head n of this group, zero beyond G
         bf16x8 qb[4];
         const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
-
-        // K -> operand order through this wave's quarter of the V tile
-        // (chunk c of local token t at chunk c ^ (t mod 8): conflict-free
-        // operand reads); the V tile is written only after every wave has
-        // read its K (barrier)
-        u32x4* kst = reinterpret_cast<u32x4*>(vs) + wave * 32 * (kHeadDim / 8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = 4 * j + lane / 16;
-            kst[t * 16 + ((lane % 16) ^ (t & 7))] = kraw[j];
-        }
-        // operands: rows 32w + 16j + n, dims 32i + 8kg (chunk 4i + kg)
         bf16x8 ka[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * j + n;
-                ka[j][i] = as_bf16x8(kst[t * 16 + ((4 * i + kg) ^ (t & 7))]);
-            }
+        k_rows_to_operands(kraw, wave, lane, vs, ka);
         __syncthreads();
 
 #pragma unroll

@@ -19,6 +19,40 @@ constexpr int kPStride = kBlock + 8;     // bf16 per P row (heads x tokens)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// K of a wavefront's 32 tokens (32w .. 32w+31 of a page) as eight
+// contiguous 1 KB loads: load j covers tokens 32w + 4j .. +3, lane l takes
+// token 32w + 4j + l/16, 16-byte chunk l % 16.  Whole lines per instruction,
+// where loading in matrix-operand order would request quarter lines.
+__device__ __forceinline__ void load_k_rows(const uint16_t* __restrict__ kp, int wave, int lane,
+                                            u32x4 (&kraw)[8]) {
+    const u32x4* kp4 = reinterpret_cast<const u32x4*>(kp) + 32 * wave * (kHeadDim / 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kraw[j] = ld16_stream(kp4 + kWave * j + lane);
+}
+
+// The loaded rows -> 16x16x32 A operands (rows 32w + 16j + n, dims 32i + 8kg,
+// i.e. 16-byte chunk 4i + kg) through this wavefront's 8 KB quarter of the V
+// tile: chunk c of local token t sits at chunk c ^ (t mod 8), so both the
+// stores and the operand reads are free of bank conflicts.  The caller puts
+// a barrier between this and the V tile's own stores.
+__device__ __forceinline__ void k_rows_to_operands(const u32x4 (&kraw)[8], int wave, int lane,
+                                                   uint16_t* vs, bf16x8 (&ka)[2][4]) {
+    u32x4* kst = reinterpret_cast<u32x4*>(vs) + wave * 32 * (kHeadDim / 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = 4 * j + lane / 16;
+        kst[t * 16 + ((lane % 16) ^ (t & 7))] = kraw[j];
+    }
+    const int n = lane % 16, kg = lane / 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * j + n;
+            ka[j][i] = as_bf16x8(kst[t * 16 + ((4 * i + kg) ^ (t & 7))]);
+        }
+}
+
 struct DecodeShared {
     uint16_t vs[kBlock * kHeadDim];
     uint16_t pl[kMaxGroup * kPStride];

@@ -86,12 +86,13 @@ void dense_decode_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
             const int tok = tid / 16 + 16 * it;
             vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
         }
+        // K: contiguous loads, operand order through the V tile (barrier
+        // before V overwrites it)
+        u32x4 kraw[8];
+        load_k_rows(kp, wave, lane, kraw);
         bf16x8 ka[2][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ka[j][i] = as_bf16x8(ld16_stream(kp + (32 * wave + 16 * j + n) * kHeadDim + 32 * i + 8 * kg));
+        k_rows_to_operands(kraw, wave, lane, sh.vs, ka);
+        __syncthreads();
 #pragma unroll
         for (int it = 0; it < 8; ++it)
             *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];

@@ -704,28 +704,25 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int n = lane % 16;   // row (B / result column) or row of A
     const int kg = lane / 16;  // lane group
 
-    // V -> LDS (tokens at or past nv are zero), K -> A operands of this
-    // wavefront's tokens 32w + 16j + n, dims 32i + 8kg
+    // K -> A operands of this wavefront's tokens 32w + 16j + n, dims 32i + 8kg
+    // (contiguous loads, operand order through the V tile; tokens past nv
+    // are read from the page's padding and masked to -inf later), then
+    // V -> LDS (tokens at or past nv are zero)
+    bf16x8 ka[2][4];
     {
-        u32x4 vv[8];
+        u32x4 vv[8], kraw[8];
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int tok = tid / 16 + 16 * it;
             vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
         }
+        load_k_rows(kp, wave, lane, kraw);
+        k_rows_to_operands(kraw, wave, lane, sh.vs, ka);
+        __syncthreads();
 #pragma unroll
         for (int it = 0; it < 8; ++it)
             *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
     }
-    bf16x8 ka[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 32 * wave + 16 * j + n;
-            ka[j][i] = as_bf16x8(tok < nv ? ld16_stream(kp + tok * kHeadDim + 32 * i + 8 * kg)
-                                          : u32x4{0u, 0u, 0u, 0u});
-        }
 
     const int nrows = cnt * G;
     for (int r0 = 0; r0 < nrows; r0 += 16) {
