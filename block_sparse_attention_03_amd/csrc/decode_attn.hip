@@ -54,35 +54,34 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
     const int n = lane % 16;   // head column (B / result) or row of A
     const int kg = lane / 16;  // lane group
 
-    // V -> LDS row-major with coalesced 16-byte loads (16 lanes per 256-byte
-    // row); tokens at or past nv are zero so that P = 0 there never meets a
-    // non-finite V.
+    // Loads in the order their data is needed -- Q, this wavefront's K, then
+    // V -- since vector loads retire in issue order: the scores and the
+    // softmax below wait only for Q and K while V is still arriving.
+    bf16x8 qb[4];  // head n of this group, zero beyond G
     {
-        u32x4 vv[8];
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int tok = tid / 16 + 16 * it;
-            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
-        }
-        // K of this wave's 32 tokens: contiguous loads, then operand order
-        // through the V tile, which is written only after every wave has read
-        // its K (barrier)
-        u32x4 kraw[8];
-        load_k_rows(kp, wave, lane, kraw);
-        // Q operands: head n of this group, zero beyond G
-        bf16x8 qb[4];
         const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
-        bf16x8 ka[2][4];
-        k_rows_to_operands(kraw, wave, lane, vs, ka);
-        __syncthreads();
-
+    }
+    // K of this wave's 32 tokens: contiguous loads, then operand order
+    // through this wave's quarter of the V tile
+    u32x4 kraw[8];
+    load_k_rows(kp, wave, lane, kraw);
+    // V rows with coalesced 16-byte loads (16 lanes per 256-byte row).  The
+    // whole page is loaded -- a page is always allocated in full, and
+    // unconditional loads keep the compiler from waiting on them early --
+    // and tokens at or past nv are zeroed when V is written to LDS, so that
+    // P = 0 there never meets a non-finite V.
+    u32x4 vv[8];
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
-            *reinterpret_cast<u32x4*>(vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
-
+    for (int it = 0; it < 8; ++it)
+        vv[it] = ld16_stream(vp + (tid / 16 + 16 * it) * kHeadDim + 8 * (tid % 16));
+    // keep every load issued here, ahead of the first wait
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ka[2][4];
+    k_rows_to_operands(kraw, wave, lane, vs, ka);
+    {
         // S^T = K Q^T for tokens 32w + 16j + 4kg + rr, head n
         f32x4 sacc[2];
 #pragma unroll
@@ -103,6 +102,7 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
         if (kg == 0) red_max[wave][n] = mx;
+        // the maxima are visible and every wave has read its K out of the V tile
         __syncthreads();
         const float m = fmaxf(fmaxf(red_max[0][n], red_max[1][n]), fmaxf(red_max[2][n], red_max[3][n]));
         // P = exp(scale * (s - m)) rounded to bf16; the sum uses the rounded values
@@ -125,6 +125,12 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
             u32x2 w2 = {static_cast<uint32_t>(pb[j][0]) | (static_cast<uint32_t>(pb[j][1]) << 16),
                         static_cast<uint32_t>(pb[j][2]) | (static_cast<uint32_t>(pb[j][3]) << 16)};
             *reinterpret_cast<u32x2*>(pl + n * kPStride + tok) = w2;
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int tok = tid / 16 + 16 * it;
+            *reinterpret_cast<u32x4*>(vs + vs_off(tok, 8 * (tid % 16))) =
+                (tok < nv) ? vv[it] : u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
 
