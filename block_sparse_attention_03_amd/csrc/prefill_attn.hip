@@ -285,25 +285,45 @@ void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offse
 // LDS words (at most kSmallMapSel selections); ranks within a bucket come
 // from the LDS atomics.  Only the nonempty buckets' counts and offsets are
 // written to the workspace: they are the only ones the attention kernels
-// read.
+// read.  A single workgroup pays every memory latency in full, so each
+// thread loads its selections once, all together, and scans a run of
+// buckets that is a whole number of 16-byte LDS chunks (no word shared with
+// another thread, so the offsets go back with plain stores).
 constexpr int kSmallMapBuckets = 49152;
 constexpr int kSmallMapSel = 16384;
+constexpr int kSmallMapThreads = 1024;
+constexpr int kSmallSelPer = kSmallMapSel / kSmallMapThreads;              // selections per thread
+constexpr int kSmallChunks = kSmallMapBuckets / kSmallMapThreads / 8;      // 16-byte chunks per thread
 
-__global__ __launch_bounds__(1024)
+__global__ __launch_bounds__(kSmallMapThreads)
 void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
                               PrefillWs w, int total_q, int B, int Hkv, int maxblk,
                               int small_cnt) {
-    __shared__ uint32_t cnt2[kSmallMapBuckets / 2];  // two 16-bit counts (later offsets) per word
+    __shared__ __attribute__((aligned(16))) uint32_t cnt2[kSmallMapBuckets / 2];  // two 16-bit counts (later offsets) per word
     __shared__ uint16_t rank[kSmallMapSel];
     __shared__ int seq_of[kSmallMapSel / kTopK];      // query token -> sequence
-    __shared__ int wsum[3][1024 / kWave];
+    __shared__ int wsum[3][kSmallMapThreads / kWave];
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
     const int NB = B * Hkv * maxblk;
     const int n_sel = total_q * Hkv * kTopK;
-    for (int i = tid; i < (NB + 1) / 2; i += 1024) cnt2[i] = 0u;
-    for (int sq = tid; sq < B; sq += 1024)
+    if (n_sel <= 0) return;  // uniform
+
+    // this thread's selections e = tid + 1024 k, loaded together (clamped
+    // indices keep every load in bounds; the copies past n_sel are unused)
+    int selv[kSmallSelPer];
+#pragma unroll
+    for (int k = 0; k < kSmallSelPer; ++k)
+        selv[k] = sel[min(tid + kSmallMapThreads * k, n_sel - 1)];
+    // buckets [a, a + per) of this thread: per is a multiple of 8
+    const int per = (ceil_div(NB, kSmallMapThreads) + 7) & ~7;  // <= 48
+    const int a = tid * per;
+    u32x4* cnt4 = reinterpret_cast<u32x4*>(cnt2);
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+        if (8 * c < per) cnt4[a / 8 + c] = u32x4{0u, 0u, 0u, 0u};
+    for (int sq = tid; sq < B; sq += kSmallMapThreads)
         for (int t = cu_q[sq]; t < cu_q[sq + 1]; ++t) seq_of[t] = sq;
     __syncthreads();
 
@@ -313,9 +333,11 @@ void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __
         const int g = (e / kTopK) % Hkv;
         return (seq_of[t] * Hkv + g) * maxblk + b;
     };
-    for (int e = tid; e < n_sel; e += 1024) {
-        const int b = sel[e];
-        if (b >= 0 && b < maxblk) {
+#pragma unroll
+    for (int k = 0; k < kSmallSelPer; ++k) {
+        const int e = tid + kSmallMapThreads * k;
+        const int b = selv[k];
+        if (e < n_sel && b >= 0 && b < maxblk) {
             const int bk = bucket_of(e, b);
             const int sh = 16 * (bk & 1);
             const uint32_t old = atomicAdd(&cnt2[bk >> 1], 1u << sh);
@@ -324,14 +346,20 @@ void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __
     }
     __syncthreads();
 
-    // scan: thread tid takes buckets [a, e); wavefront prefix sums, then the
-    // 16 wavefront totals through LDS
-    const int per = ceil_div(NB, 1024);
-    const int a = min(NB, tid * per), e_end = min(NB, a + per);
-    auto count_at = [&](int i) { return (int)((cnt2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
+    // scan: this thread's counts in registers (16-byte LDS reads), totals,
+    // wavefront prefix sums, then the 16 wavefront totals through LDS
+    uint32_t cw[4 * kSmallChunks];
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+        const u32x4 v = (8 * c < per) ? cnt4[a / 8 + c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) cw[4 * c + x] = v[x];
+    }
+    auto cnt_of = [&](int j) { return (int)((cw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu); };
     int sum = 0, nl = 0, ns = 0;
-    for (int i = a; i < e_end; ++i) {
-        const int c = count_at(i);
+#pragma unroll
+    for (int j = 0; j < 8 * kSmallChunks; ++j) {
+        const int c = cnt_of(j);  // zero past per and past NB
         sum += c;
         nl += c > small_cnt;
         ns += c > 0 && c <= small_cnt;
@@ -359,8 +387,9 @@ void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __
         runl += wsum[1][k];
         runs += wsum[2][k];
     }
-    for (int i = a; i < e_end; ++i) {
-        const int c = count_at(i);
+    // nonempty buckets -> workspace; counts -> exclusive offsets, word by
+    // word in the same registers, then back to LDS
+    auto emit = [&](int i, int c) {
         if (c > 0) {
             w.counts[i] = c;
             w.offsets[i] = run;
@@ -369,32 +398,35 @@ void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __
             else
                 w.small[1 + runs++] = i;
         }
+        const int o = run;
         run += c;
+        return (uint32_t)o;
+    };
+#pragma unroll 2
+    for (int x = 0; x < 4 * kSmallChunks; ++x) {
+        const uint32_t o0 = emit(a + 2 * x, (int)(cw[x] & 0xFFFFu));
+        const uint32_t o1 = emit(a + 2 * x + 1, (int)(cw[x] >> 16));
+        cw[x] = o0 | (o1 << 16);
     }
-    if (tid == 1023) {
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+        if (8 * c < per) cnt4[a / 8 + c] = u32x4{cw[4 * c], cw[4 * c + 1], cw[4 * c + 2], cw[4 * c + 3]};
+    if (tid == kSmallMapThreads - 1) {
         w.buckets[0] = runl;
         w.small[0] = runs;
-    }
-    __syncthreads();  // every count has been read
-    // counts -> exclusive offsets in place (each thread its own buckets)
-    run = isum - sum;
-    for (int k = 0; k < wave; ++k) run += wsum[0][k];
-    for (int i = a; i < e_end; ++i) {
-        const int c = count_at(i);
-        atomicAnd(&cnt2[i >> 1], ~(0xFFFFu << (16 * (i & 1))));
-        atomicOr(&cnt2[i >> 1], (uint32_t)run << (16 * (i & 1)));
-        run += c;
     }
     __syncthreads();
 
     // place: entries[offset + rank] = query << 4 | slot
-    for (int e = tid; e < n_sel; e += 1024) {
-        const int b = sel[e];
-        if (b >= 0 && b < maxblk) {
+    auto off_at = [&](int i) { return (int)((cnt2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
+#pragma unroll
+    for (int k = 0; k < kSmallSelPer; ++k) {
+        const int e = tid + kSmallMapThreads * k;
+        const int b = selv[k];
+        if (e < n_sel && b >= 0 && b < maxblk) {
             const int bk = bucket_of(e, b);
-            const int off = count_at(bk);
             const int t = e / (Hkv * kTopK);
-            w.entries[off + rank[e]] = (t << 4) | (e % kTopK);
+            w.entries[off_at(bk) + rank[e]] = (t << 4) | (e % kTopK);
         }
     }
 }
@@ -892,7 +924,7 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     // buckets of at most small_cnt entries (kSmallRows rows) are small
     const int small_cnt = kSmallRows / (s.Hq / s.Hkv);
     if (NB <= kSmallMapBuckets && (int64_t)total_q * s.Hkv * kTopK <= kSmallMapSel) {
-        hipLaunchKernelGGL(inverse_map_small_kernel, dim3(1), dim3(1024), 0, st, sel, cu_q, w,
+        hipLaunchKernelGGL(inverse_map_small_kernel, dim3(1), dim3(kSmallMapThreads), 0, st, sel, cu_q, w,
                            total_q, s.B, s.Hkv, s.maxblk, small_cnt);
     } else {
         hipLaunchKernelGGL(zero_kernel, dim3(min(1024, ceil_div(NB, 256))), dim3(256), 0, st,

@@ -257,6 +257,44 @@ def test_quantised_scores_tie_at_the_threshold(ctx, n_heads):
     assert torch.equal(fused.lse, ref.lse)
 
 
+def _step_into(step, ws):
+    """msa_decode_step on step's inputs, into step's outputs, with workspace ws."""
+    x = step.x
+    L.msa_decode_step(step.dims, x.q_idx, x.kidx_cache, x.q, x.k_cache, x.v_cache,
+                      x.block_table, x.seq_lens, step.out, step.lse, step.sel, ws)
+
+
+def test_fused_decode_step_shares_a_workspace_across_shapes():
+    """One workspace (uninitialised, sized for the largest shape) serves calls
+    of different shapes in turn: each call, with its outputs poisoned first,
+    equals the four calls."""
+    cfgs = [gen.MsaConfig("ws_a", [9000, 3000, 700], [1, 1, 1], 12, 3, permute_pages=True,
+                          seed=61),
+            gen.MsaConfig("ws_b", [(41 * i * i) % 30000 + 90 for i in range(12)], [1] * 12, 48, 8,
+                          permute_pages=True, seed=62),
+            gen.MsaConfig("ws_c", [129, 50000], [1, 1], 16, 2, permute_pages=True, seed=63)]
+    cases = []
+    for cfg in cfgs:
+        x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+        ref = MsaStep(x)
+        ref.run()
+        cases.append((cfg, MsaStep(x, fused=True), ref))
+    torch.cuda.synchronize()
+    nbytes = max(L.msa_decode_step_workspace_size(c[1].dims) for c in cases)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    for i, k in enumerate([0, 1, 0, 2, 1, 2, 0]):
+        cfg, step, ref = cases[k]
+        print(f"[shared-ws] call {i}: {cfg.name}", flush=True)
+        step.out.fill_(float("nan"))
+        step.lse.fill_(float("nan"))
+        step.sel.fill_(-7)
+        _step_into(step, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, ref.out), f"call {i} ({cfg.name}): out"
+        assert torch.equal(step.lse, ref.lse), f"call {i} ({cfg.name}): lse"
+        assert torch.equal(step.sel, ref.sel), f"call {i} ({cfg.name}): sel"
+
+
 def test_fused_decode_step_rows_past_8192_blocks():
     """Rows of more than 8192 blocks select in the standalone kernel inside
     msa_decode_step; the result still equals the four calls."""
