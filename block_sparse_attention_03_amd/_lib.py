@@ -2,9 +2,10 @@
 
 Argument marshalling only: every function checks the tensors it is given
 (device, dtype, contiguity, shape), packs ``msa_dims_t`` and calls the C entry
-point of the same name on the current HIP stream.  All arithmetic runs in the
-library's HIP kernels; there is no CPU fallback, and loading fails loudly when
-the library has not been built.
+point of the same name on the current HIP stream; ``prepare_<name>`` does the
+checking and packing once and returns a PreparedCall that repeats the call.
+All arithmetic runs in the library's HIP kernels; there is no CPU fallback,
+and loading fails loudly when the library has not been built.
 """
 from __future__ import annotations
 
@@ -147,27 +148,60 @@ def _check(status: int, where: str):
 BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
 
 
-def msa_index_score(dims, total_q, q_idx, kidx_cache, block_table, seq_lens, cu_q, scores,
-                    stream=None):
+class PreparedCall:
+    """One entry point with its tensors checked and its arguments packed once.
+    Calling it passes the same pointers again on the current (or a given) HIP
+    stream: for loops that reuse their buffers (decode layers, benchmarks),
+    where checking every tensor on every call would cost more host time than
+    the kernels take on the GPU.  The tensors are referenced here, so their
+    storage stays allocated; their contents may change between calls."""
+    __slots__ = ("_fn", "_args", "_where", "_keep")
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream)), self._where)
+
+
+def prepare_msa_index_score(dims, total_q, q_idx, kidx_cache, block_table, seq_lens, cu_q, scores):
+    """msa_index_score with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     H, B, W = d.num_kv_heads, d.num_seqs, d.max_blocks_per_seq
     args = (_ptr(q_idx, BF16, "q_idx", (total_q, H, d.idx_dim)),
             _ptr(kidx_cache, BF16, "kidx_cache", (d.num_pages, d.num_idx_heads, d.block_size, d.idx_dim)),
             _ptr(block_table, I32, "block_table", (B, W)), _ptr(seq_lens, I32, "seq_lens", (B,)),
             _ptr(cu_q, I32, "cu_q", (B + 1,)), _ptr(scores, F32, "scores", (total_q, H, W)))
-    _check(lib().msa_index_score(ctypes.byref(d), total_q, *args, _stream(stream)), "msa_index_score")
+    return PreparedCall(lib().msa_index_score, (ctypes.byref(d), total_q, *args), "msa_index_score",
+                        (d, q_idx, kidx_cache, block_table, seq_lens, cu_q, scores))
 
 
-def msa_topk_blocks(dims, total_q, scores, seq_lens, cu_q, sel, stream=None):
+def msa_index_score(dims, total_q, q_idx, kidx_cache, block_table, seq_lens, cu_q, scores,
+                    stream=None):
+    prepare_msa_index_score(dims, total_q, q_idx, kidx_cache, block_table, seq_lens, cu_q,
+                            scores)(stream)
+
+
+def prepare_msa_topk_blocks(dims, total_q, scores, seq_lens, cu_q, sel):
+    """msa_topk_blocks with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     H, B = d.num_kv_heads, d.num_seqs
     args = (_ptr(scores, F32, "scores", (total_q, H, d.max_blocks_per_seq)),
             _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
             _ptr(sel, I32, "sel", (total_q, H, d.topk)))
-    _check(lib().msa_topk_blocks(ctypes.byref(d), total_q, *args, _stream(stream)), "msa_topk_blocks")
+    return PreparedCall(lib().msa_topk_blocks, (ctypes.byref(d), total_q, *args), "msa_topk_blocks",
+                        (d, scores, seq_lens, cu_q, sel))
 
 
-def msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens, stream=None):
+def msa_topk_blocks(dims, total_q, scores, seq_lens, cu_q, sel, stream=None):
+    prepare_msa_topk_blocks(dims, total_q, scores, seq_lens, cu_q, sel)(stream)
+
+
+def prepare_msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens):
+    """msa_build_page_table with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, H = d.num_seqs, d.num_kv_heads
     args = (_ptr(sel, I32, "sel", (B, H, d.topk)),
@@ -175,8 +209,13 @@ def msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens,
             _ptr(seq_lens, I32, "seq_lens", (B,)),
             _ptr(page_table, I32, "page_table", (B * H, d.topk)),
             _ptr(row_lens, I32, "row_lens", (B * H,)))
-    _check(lib().msa_build_page_table(ctypes.byref(d), *args, _stream(stream)),
-           "msa_build_page_table")
+    return PreparedCall(lib().msa_build_page_table, (ctypes.byref(d), *args),
+                        "msa_build_page_table",
+                        (d, sel, block_table, seq_lens, page_table, row_lens))
+
+
+def msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens, stream=None):
+    prepare_msa_build_page_table(dims, sel, block_table, seq_lens, page_table, row_lens)(stream)
 
 
 def msa_decode_workspace_size(dims) -> int:
@@ -187,8 +226,10 @@ def msa_prefill_workspace_size(dims, total_q) -> int:
     return int(lib().msa_prefill_workspace_size(ctypes.byref(dims), total_q))
 
 
-def msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out, lse, workspace,
-                           stream=None):
+def prepare_msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out, lse,
+                                   workspace):
+    """msa_sparse_attn_decode with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
     cache = (d.num_pages, H, d.block_size, d.head_dim)
@@ -200,12 +241,21 @@ def msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out,
             _ptr(lse, F32, "lse", (B, Hq)) if lse is not None else None,
             _ptr(workspace, torch.uint8, "workspace"))
     nbytes = workspace.numel() if workspace is not None else 0
-    _check(lib().msa_sparse_attn_decode(ctypes.byref(d), *args, nbytes, _stream(stream)),
-           "msa_sparse_attn_decode")
+    return PreparedCall(lib().msa_sparse_attn_decode, (ctypes.byref(d), *args, nbytes),
+                        "msa_sparse_attn_decode",
+                        (d, q, k_cache, v_cache, page_table, row_lens, out, lse, workspace))
 
 
-def msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel,
-                            out, lse, workspace, stream=None):
+def msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out, lse, workspace,
+                           stream=None):
+    prepare_msa_sparse_attn_decode(dims, q, k_cache, v_cache, page_table, row_lens, out, lse,
+                                   workspace)(stream)
+
+
+def prepare_msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                                    sel, out, lse, workspace):
+    """msa_sparse_attn_prefill with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
     cache = (d.num_pages, H, d.block_size, d.head_dim)
@@ -218,16 +268,26 @@ def msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq
             _ptr(lse, F32, "lse", (total_q, Hq)) if lse is not None else None,
             _ptr(workspace, torch.uint8, "workspace"))
     nbytes = workspace.numel() if workspace is not None else 0
-    _check(lib().msa_sparse_attn_prefill(ctypes.byref(d), total_q, *args, nbytes, _stream(stream)),
-           "msa_sparse_attn_prefill")
+    return PreparedCall(lib().msa_sparse_attn_prefill, (ctypes.byref(d), total_q, *args, nbytes),
+                        "msa_sparse_attn_prefill",
+                        (d, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, out, lse,
+                         workspace))
+
+
+def msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel,
+                            out, lse, workspace, stream=None):
+    prepare_msa_sparse_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                                    sel, out, lse, workspace)(stream)
 
 
 def msa_decode_step_workspace_size(dims) -> int:
     return int(lib().msa_decode_step_workspace_size(ctypes.byref(dims)))
 
 
-def msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out, lse,
-                    sel, workspace, stream=None):
+def prepare_msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens,
+                            out, lse, sel, workspace):
+    """msa_decode_step with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
     cache = (d.num_pages, H, d.block_size, d.head_dim)
@@ -242,16 +302,25 @@ def msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, s
             _ptr(sel, I32, "sel", (B, H, d.topk)) if sel is not None else None,
             _ptr(workspace, torch.uint8, "workspace"))
     nbytes = workspace.numel() if workspace is not None else 0
-    _check(lib().msa_decode_step(ctypes.byref(d), *args, nbytes, _stream(stream)), "msa_decode_step")
+    return PreparedCall(lib().msa_decode_step, (ctypes.byref(d), *args, nbytes), "msa_decode_step",
+                        (d, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
+                         lse, sel, workspace))
+
+
+def msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                    sel, workspace, stream=None):
+    prepare_msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens,
+                            out, lse, sel, workspace)(stream)
 
 
 def msa_dense_decode_workspace_size(dims) -> int:
     return int(lib().msa_dense_decode_workspace_size(ctypes.byref(dims)))
 
 
-def msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace,
-                          stream=None):
-    """Dense GQA decode over every cached token (the comparison baseline)."""
+def prepare_msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                                  workspace):
+    """msa_dense_attn_decode with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
     cache = (d.num_pages, H, d.block_size, d.head_dim)
@@ -263,13 +332,22 @@ def msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out,
             _ptr(lse, F32, "lse", (B, Hq)) if lse is not None else None,
             _ptr(workspace, torch.uint8, "workspace"))
     nbytes = workspace.numel() if workspace is not None else 0
-    _check(lib().msa_dense_attn_decode(ctypes.byref(d), *args, nbytes, _stream(stream)),
-           "msa_dense_attn_decode")
+    return PreparedCall(lib().msa_dense_attn_decode, (ctypes.byref(d), *args, nbytes),
+                        "msa_dense_attn_decode",
+                        (d, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace))
 
 
-def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, out,
-                           lse, stream=None):
-    """Dense causal attention over every cached token (the prefill baseline)."""
+def msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace,
+                          stream=None):
+    """Dense GQA decode over every cached token (the comparison baseline)."""
+    prepare_msa_dense_attn_decode(dims, q, k_cache, v_cache, block_table, seq_lens, out, lse,
+                                  workspace)(stream)
+
+
+def prepare_msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                                   out, lse):
+    """msa_dense_attn_prefill with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
     cache = (d.num_pages, H, d.block_size, d.head_dim)
@@ -279,21 +357,35 @@ def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_
             _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
             _ptr(out, BF16, "out", (total_q, Hq, d.head_dim)),
             _ptr(lse, F32, "lse", (total_q, Hq)) if lse is not None else None)
-    _check(lib().msa_dense_attn_prefill(ctypes.byref(d), total_q, *args, _stream(stream)),
-           "msa_dense_attn_prefill")
+    return PreparedCall(lib().msa_dense_attn_prefill, (ctypes.byref(d), total_q, *args),
+                        "msa_dense_attn_prefill",
+                        (d, q, k_cache, v_cache, block_table, seq_lens, cu_q, out, lse))
+
+
+def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q, out,
+                           lse, stream=None):
+    """Dense causal attention over every cached token (the prefill baseline)."""
+    prepare_msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                                   out, lse)(stream)
 
 
 MSA_FAULT_SEQ_LEN, MSA_FAULT_CU_Q, MSA_FAULT_BLOCK_TABLE = 1, 2, 4
 
 
-def msa_validate_inputs(dims, total_q, block_table, seq_lens, cu_q, status, stream=None):
-    """Device-side check of the content preconditions; `status` (one int32 on
-    the device) receives 0 or the OR of the MSA_FAULT_* bits found."""
+def prepare_msa_validate_inputs(dims, total_q, block_table, seq_lens, cu_q, status):
+    """msa_validate_inputs with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
     d = dims
     B = d.num_seqs
     args = (_ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
             _ptr(seq_lens, I32, "seq_lens", (B,)),
             _ptr(cu_q, I32, "cu_q", (B + 1,)) if cu_q is not None else None,
             _ptr(status, I32, "status", (1,)))
-    _check(lib().msa_validate_inputs(ctypes.byref(d), total_q, *args, _stream(stream)),
-           "msa_validate_inputs")
+    return PreparedCall(lib().msa_validate_inputs, (ctypes.byref(d), total_q, *args),
+                        "msa_validate_inputs", (d, block_table, seq_lens, cu_q, status))
+
+
+def msa_validate_inputs(dims, total_q, block_table, seq_lens, cu_q, status, stream=None):
+    """Device-side check of the content preconditions; `status` (one int32 on
+    the device) receives 0 or the OR of the MSA_FAULT_* bits found."""
+    prepare_msa_validate_inputs(dims, total_q, block_table, seq_lens, cu_q, status)(stream)

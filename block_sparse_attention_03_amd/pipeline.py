@@ -42,36 +42,44 @@ class MsaStep:
             raise L.MsaError(L.MSA_ERROR_NOT_SUPPORTED, "workspace size")
         self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
+        # every call's arguments checked and packed once (the buffers above
+        # and the inputs' tensors are reused by every run)
+        self._score = L.prepare_msa_index_score(self.dims, T, x.q_idx, x.kidx_cache,
+                                                x.block_table, x.seq_lens, x.cu_q, self.scores)
+        self._topk = L.prepare_msa_topk_blocks(self.dims, T, self.scores, x.seq_lens, x.cu_q,
+                                               self.sel)
+        if self.fused:
+            self._fused = L.prepare_msa_decode_step(self.dims, x.q_idx, x.kidx_cache, x.q,
+                                                    x.k_cache, x.v_cache, x.block_table,
+                                                    x.seq_lens, self.out, self.lse, self.sel,
+                                                    self.workspace)
+        elif self.decode:
+            self._page_table = L.prepare_msa_build_page_table(self.dims, self.sel, x.block_table,
+                                                              x.seq_lens, self.page_table,
+                                                              self.row_lens)
+            self._attend = L.prepare_msa_sparse_attn_decode(self.dims, x.q, x.k_cache, x.v_cache,
+                                                            self.page_table, self.row_lens,
+                                                            self.out, self.lse, self.workspace)
+        else:
+            self._attend = L.prepare_msa_sparse_attn_prefill(self.dims, T, x.q, x.k_cache,
+                                                             x.v_cache, x.block_table, x.seq_lens,
+                                                             x.cu_q, self.sel, self.out, self.lse,
+                                                             self.workspace)
+
     def score(self, stream=None):
-        x = self.x
-        L.msa_index_score(self.dims, self.cfg.total_q, x.q_idx, x.kidx_cache, x.block_table,
-                          x.seq_lens, x.cu_q, self.scores, stream)
+        self._score(stream)
 
     def topk(self, stream=None):
-        x = self.x
-        L.msa_topk_blocks(self.dims, self.cfg.total_q, self.scores, x.seq_lens, x.cu_q, self.sel,
-                          stream)
+        self._topk(stream)
 
     def page_table_step(self, stream=None):
-        x = self.x
-        L.msa_build_page_table(self.dims, self.sel, x.block_table, x.seq_lens, self.page_table,
-                               self.row_lens, stream)
+        self._page_table(stream)
 
     def attend(self, stream=None):
-        x = self.x
-        if self.decode:
-            L.msa_sparse_attn_decode(self.dims, x.q, x.k_cache, x.v_cache, self.page_table,
-                                     self.row_lens, self.out, self.lse, self.workspace, stream)
-        else:
-            L.msa_sparse_attn_prefill(self.dims, self.cfg.total_q, x.q, x.k_cache, x.v_cache,
-                                      x.block_table, x.seq_lens, x.cu_q, self.sel, self.out,
-                                      self.lse, self.workspace, stream)
+        self._attend(stream)
 
     def fused_step(self, stream=None):
-        x = self.x
-        L.msa_decode_step(self.dims, x.q_idx, x.kidx_cache, x.q, x.k_cache, x.v_cache,
-                          x.block_table, x.seq_lens, self.out, self.lse, self.sel, self.workspace,
-                          stream)
+        self._fused(stream)
 
     def run(self, stream=None):
         if self.fused:
