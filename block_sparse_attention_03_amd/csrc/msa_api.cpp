@@ -66,6 +66,7 @@ msa_status_t msa_index_score(const msa_dims_t* dims, int32_t total_q, const uint
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
     if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q_idx || !kidx_cache || !block_table || !seq_lens || !cu_q || !scores)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q_idx, 16) || !aligned(kidx_cache, 16) || !aligned(block_table, 4) ||
@@ -83,6 +84,7 @@ msa_status_t msa_topk_blocks(const msa_dims_t* dims, int32_t total_q, const floa
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
     if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!scores || !seq_lens || !cu_q || !sel) return MSA_ERROR_INVALID_VALUE;
     if (!aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(cu_q, 4) || !aligned(sel, 4))
         return MSA_ERROR_INVALID_VALUE;
@@ -96,6 +98,7 @@ msa_status_t msa_build_page_table(const msa_dims_t* dims, const int32_t* sel,
     MsaShape s;
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
+    if (s.B == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!sel || !block_table || !seq_lens || !page_table || !row_lens) return MSA_ERROR_INVALID_VALUE;
     if (!aligned(sel, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
         !aligned(page_table, 4) || !aligned(row_lens, 4))
@@ -124,6 +127,7 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t* dims, const uint16_t* q,
     MsaShape s;
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
+    if (s.B == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q || !k_cache || !v_cache || !page_table || !row_lens || !out) return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(page_table, 4) || !aligned(row_lens, 4) || !aligned(out, 16) ||
@@ -145,6 +149,7 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t* dims, int32_t total_q, co
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
     if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_q || !sel || !out)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -173,6 +178,7 @@ msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
     MsaShape s;
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
+    if (s.B == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q_idx || !kidx_cache || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q_idx, 16) || !aligned(kidx_cache, 16) || !aligned(q, 16) ||
@@ -202,6 +208,7 @@ msa_status_t msa_dense_attn_decode(const msa_dims_t* dims, const uint16_t* q,
     MsaShape s;
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
+    if (s.B == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -223,6 +230,7 @@ msa_status_t msa_dense_attn_prefill(const msa_dims_t* dims, int32_t total_q, con
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
     if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_q || !out)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||

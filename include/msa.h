@@ -33,7 +33,10 @@
  *     default stream) and returns without synchronising.
  *   - Host-side checks (dims, null or misaligned pointers, workspace size) run
  *     before any launch; on failure the call returns an error status, launches
- *     nothing and leaves outputs untouched.  The library never aborts, prints
+ *     nothing and leaves outputs untouched.  A call with no work (num_seqs =
+ *     0, or total_q = 0 for the calls that take it; msa_validate_inputs
+ *     excepted) returns MSA_SUCCESS once dims and total_q pass, without
+ *     looking at its pointers (they may be NULL) or launching anything.  The library never aborts, prints
  *     or throws.  Device-resident CONTENT (seq_lens, cu_q, block_table, sel,
  *     page_table, row_lens) is a precondition the caller guarantees: page
  *     indices in [0, num_pages), 1 <= seq_lens[s], 0 <= cu_q[s+1]-cu_q[s] <=

@@ -136,12 +136,45 @@ def test_dense_prefill_errors():
     assert lib.msa_dense_attn_prefill(ctypes.byref(bad), 5, A, A, A, A, A, A, A, A, None) == L.MSA_ERROR_NOT_SUPPORTED
 
 
+def test_calls_with_no_work_succeed_without_pointers():
+    """num_seqs = 0 or total_q = 0: every compute entry point returns success
+    after the dims checks, reading no pointer (all NULL here) and launching
+    nothing -- so it runs without a GPU."""
+    lib = L.lib()
+    empty = dims(num_seqs=0)
+    some = dims()
+    N = None
+    ok = L.MSA_SUCCESS
+    for d in (ctypes.byref(empty), ctypes.byref(some)):
+        assert lib.msa_index_score(d, 0, N, N, N, N, N, N, N) == ok
+        assert lib.msa_topk_blocks(d, 0, N, N, N, N, N) == ok
+        assert lib.msa_sparse_attn_prefill(d, 0, N, N, N, N, N, N, N, N, N, N, 0, N) == ok
+        assert lib.msa_dense_attn_prefill(d, 0, N, N, N, N, N, N, N, N, N) == ok
+    d = ctypes.byref(empty)
+    assert lib.msa_build_page_table(d, N, N, N, N, N, N) == ok
+    assert lib.msa_sparse_attn_decode(d, N, N, N, N, N, N, N, N, 0, N) == ok
+    assert lib.msa_decode_step(d, N, N, N, N, N, N, N, N, N, N, N, 0, N) == ok
+    assert lib.msa_dense_attn_decode(d, N, N, N, N, N, N, N, N, 0, N) == ok
+    # work to do: the NULL pointers are refused
+    d = ctypes.byref(some)
+    assert lib.msa_index_score(d, 3, N, N, N, N, N, N, N) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_decode_step(d, N, N, N, N, N, N, N, N, N, N, N, 0, N) == L.MSA_ERROR_INVALID_VALUE
+    # invalid dims are still invalid with no work
+    bad = dims(num_seqs=0, num_q_heads=7)
+    assert lib.msa_index_score(ctypes.byref(bad), 0, N, N, N, N, N, N, N) == L.MSA_ERROR_INVALID_VALUE
+
+
 def test_binding_checks_tensors_before_calling():
     import torch
     d = dims()
     cpu = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         L.msa_index_score(d, 4, cpu, cpu, cpu, cpu, cpu, cpu)
+    # a prepared call checks its tensors when it is prepared
+    with pytest.raises(ValueError):
+        L.prepare_msa_index_score(d, 4, cpu, cpu, cpu, cpu, cpu, cpu)
+    with pytest.raises(ValueError):
+        L.prepare_msa_decode_step(d, cpu, cpu, cpu, cpu, cpu, cpu, cpu, cpu, None, None, cpu)
 
 
 def test_calibration_library_exports():

@@ -295,6 +295,32 @@ def test_fused_decode_step_shares_a_workspace_across_shapes():
         assert torch.equal(step.sel, ref.sel), f"call {i} ({cfg.name}): sel"
 
 
+def test_prepared_calls_read_current_contents():
+    """A PreparedCall passes the same pointers again: after the inputs change
+    in place, its result equals a fresh, unprepared call on the new contents
+    (and differs from the result before the change)."""
+    cfg = gen.MsaConfig("prepared", [9000, 3000, 700], [1, 1, 1], 12, 3, permute_pages=True,
+                        seed=65)
+    print(f"[prepared] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    step = MsaStep(x, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    before = step.out.clone()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x.q.copy_(torch.randn(x.q.shape, generator=g, device="cuda").to(torch.bfloat16))
+    x.q_idx.copy_(torch.randn(x.q_idx.shape, generator=g, device="cuda").to(torch.bfloat16))
+    step.run()
+    fresh = MsaStep(x, fused=True)
+    L.msa_decode_step(fresh.dims, x.q_idx, x.kidx_cache, x.q, x.k_cache, x.v_cache,
+                      x.block_table, x.seq_lens, fresh.out, fresh.lse, fresh.sel, fresh.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(step.out, fresh.out)
+    assert torch.equal(step.lse, fresh.lse)
+    assert torch.equal(step.sel, fresh.sel)
+    assert not torch.equal(step.out, before)
+
+
 def test_fused_decode_step_rows_past_8192_blocks():
     """Rows of more than 8192 blocks select in the standalone kernel inside
     msa_decode_step; the result still equals the four calls."""
