@@ -12,8 +12,10 @@
 // one 256-thread workgroup per (chunk, row) walks its pages with the online
 // softmax (running max and sum per head, output rescaled when the max grows),
 // using the same page tile as the sparse kernel: the row's G heads are the 16
-// columns of 16x16x32 bf16 matrix-core tiles, K operands come straight from
-// HBM, V is staged in LDS with coalesced loads and read back transposed.
+// columns of 16x16x32 bf16 matrix-core tiles, K arrives in contiguous pieces
+// and reaches operand order through LDS, V is staged in LDS with coalesced
+// loads and read back transposed; the next page's K and V are in flight while
+// the current page is multiplied.
 // Each chunk leaves a normalised partial output and its log-sum-exp; a second
 // kernel merges a row's chunks with the Log-Sum-Exp rule.
 #include "decode_tile.hpp"
@@ -39,7 +41,9 @@ __host__ __device__ inline DenseWs dense_ws(void* ws, int R, int chunks, int G) 
     return w;
 }
 
-__global__ __launch_bounds__(kDecThreads)
+// Three wavefronts per SIMD (at most 168 VGPRs) with the next page's K and V
+// held in registers measured faster than two with more registers.
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void dense_decode_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
                          const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
                          const uint16_t* __restrict__ v_cache,
@@ -73,29 +77,29 @@ void dense_decode_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
     float m_run = -__builtin_inff(), l_run = 0.f;  // per head n, in scaled-log2 units for m
     f32x4 o_run[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
-    for (int pi = p0; pi < p1; ++pi) {
-        const int nv = min(kBlock, L - pi * kBlock);
-        const int page = block_table[(size_t)s * maxblk + pi];
-        const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
-        const uint16_t* kp = k_cache + page_off;
-        const uint16_t* vp = v_cache + page_off;
-        __syncthreads();  // the previous page's LDS reads are done
-        u32x4 vv[8];
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int tok = tid / 16 + 16 * it;
-            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
-        }
-        // K: contiguous loads, operand order through the V tile (barrier
-        // before V overwrites it)
-        u32x4 kraw[8];
-        load_k_rows(kp, wave, lane, kraw);
-        bf16x8 ka[2][4];
-        k_rows_to_operands(kraw, wave, lane, sh.vs, ka);
-        __syncthreads();
+    // A page's K (contiguous 1 KB loads, see load_k_rows) and V (16 lanes per
+    // 256-byte row), the whole page: pages are allocated in full, and loads
+    // with no condition keep the compiler from waiting on them early.  Page
+    // i + 1 is loaded while page i is in its softmax and products; its
+    // block-table entry one page earlier still.
+    const int32_t* bt = block_table + (size_t)s * maxblk;
+    auto load_page = [&](int page, u32x4 (&kraw)[8], u32x4 (&vv)[8]) {
+        const size_t off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+        load_k_rows(k_cache + off, wave, lane, kraw);
 #pragma unroll
         for (int it = 0; it < 8; ++it)
-            *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
+            vv[it] = ld16_stream(v_cache + off + (tid / 16 + 16 * it) * kHeadDim + 8 * (tid % 16));
+    };
+    u32x4 kraw[8], vv[8];
+    load_page(bt[p0], kraw, vv);
+    int next_page = (p0 + 1 < p1) ? bt[p0 + 1] : 0;
+
+    for (int pi = p0; pi < p1; ++pi) {
+        const int nv = min(kBlock, L - pi * kBlock);
+        __syncthreads();  // the previous page's LDS reads are done
+        // K -> operands through this wavefront's quarter of the V tile
+        bf16x8 ka[2][4];
+        k_rows_to_operands(kraw, wave, lane, sh.vs, ka);
 
         // S^T = K Q^T for tokens 32w + 16j + 4kg + rr, head n
         f32x4 sacc[2];
@@ -117,7 +121,20 @@ void dense_decode_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
         mx = wave_max_xor(mx, 16);
         mx = wave_max_xor(mx, 32);
         if (kg == 0) sh.red_max[wave][n] = mx;
+        // the maxima are visible and every wavefront has read its K out of the
+        // V tile: V goes in (tokens at or past nv zero, so that P = 0 there
+        // never meets a non-finite V), and the next page's loads go out
         __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int tok = tid / 16 + 16 * it;
+            *reinterpret_cast<u32x4*>(sh.vs + vs_off(tok, 8 * (tid % 16))) =
+                (tok < nv) ? vv[it] : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (pi + 1 < p1) {  // uniform
+            load_page(next_page, kraw, vv);
+            next_page = (pi + 2 < p1) ? bt[pi + 2] : 0;
+        }
         const float m_page = fmaxf(fmaxf(sh.red_max[0][n], sh.red_max[1][n]),
                                    fmaxf(sh.red_max[2][n], sh.red_max[3][n]));
         const float m_new = fmaxf(m_run, m_page);  // finite: every page has a valid token
@@ -180,11 +197,14 @@ void dense_decode_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
     }
 }
 
-// One thread per (row, head, dim): Log-Sum-Exp merge of the row's chunks.
+// One thread per (row, head, dim): Log-Sum-Exp merge of the row's chunks (at
+// most kDenseMaxChunks), every chunk's partial loaded together.
+constexpr int kDenseMaxChunks = 64;
 __global__ __launch_bounds__(kHeadDim)
 void dense_merge_kernel(const int32_t* __restrict__ seq_lens, const void* __restrict__ ws,
                         uint16_t* __restrict__ out, float* __restrict__ lse_out, int Hq, int Hkv,
                         int R, int chunk, int chunks) {
+    __shared__ float lse_s[kDenseMaxChunks];
     const int rn = blockIdx.x;  // r * G + n
     const int G = Hq / Hkv;
     const int r = rn / G;
@@ -192,16 +212,24 @@ void dense_merge_kernel(const int32_t* __restrict__ seq_lens, const void* __rest
     const int d = threadIdx.x;
     const int s = r / Hkv;
     const int used = ceil_div(ceil_div(seq_lens[s], kBlock), chunk);  // chunks with pages
+    const int last = max(used, 1) - 1;  // clamped index: every load in bounds
     DenseWs w = dense_ws(const_cast<void*>(ws), R, chunks, G);
     const float* lp = w.lse + (size_t)r * chunks * G + n;
     const float* op = w.o + ((size_t)r * chunks * G + n) * kHeadDim + d;
+    float oi[kDenseMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kDenseMaxChunks; ++i) oi[i] = op[(size_t)min(i, last) * G * kHeadDim];
+    if (d < kDenseMaxChunks) lse_s[d] = lp[(size_t)min(d, last) * G];
+    __syncthreads();
     float mx = -__builtin_inff();
-    for (int i = 0; i < used; ++i) mx = fmaxf(mx, lp[(size_t)i * G]);
+#pragma unroll
+    for (int i = 0; i < kDenseMaxChunks; ++i) mx = (i < used) ? fmaxf(mx, lse_s[i]) : mx;
     float den = 0.f, acc = 0.f;
-    for (int i = 0; i < used; ++i) {
-        const float wi = __expf(lp[(size_t)i * G] - mx);
-        den += wi;
-        acc += wi * op[(size_t)i * G * kHeadDim];
+#pragma unroll
+    for (int i = 0; i < kDenseMaxChunks; ++i) {
+        const float wi = __expf(lse_s[i] - mx);
+        den = (i < used) ? den + wi : den;
+        acc = (i < used) ? __builtin_fmaf(wi, oi[i], acc) : acc;
     }
     const int h = (r % Hkv) * G + n;
     out[((size_t)s * Hq + h) * kHeadDim + d] = f32_to_bf16(acc / den);
