@@ -274,35 +274,44 @@ hipError_t msa_launch_dense_decode(const MsaShape& s, const uint16_t* q, const u
 // ---------------------------------------------------------------------------
 //
 // Query token t of sequence s (position p = L_s - nq_s + (t - q0_s)) attends
-// every cached token j <= p of its group.  One 256-thread workgroup owns 128
-// (query, head) rows of one (sequence, group) -- four 32-row tiles, one per
+// every cached token j <= p of its group.  One 512-thread workgroup owns 256
+// (query, head) rows of one (sequence, group) -- eight 32-row tiles, one per
 // wavefront, rows ordered query-major with the group's G heads adjacent -- and
-// walks the KV blocks 0 .. (its last row's own block), staging each block's K
-// and V in LDS once for all its rows.  Per block and tile: S^T = K Q^T with
-// 32x32x16 bf16 products, the causal cut where a row's own block is reached,
-// the online softmax (running max and sum per row, accumulators rescaled),
-// P rounded to bf16 as the B operand of O^T += V^T P^T with V^T from LDS
-// transpose reads.  The staging tiles for the query gather and the output
-// store share the K/V region, so two workgroups fit in a compute unit: one
-// computes while the other stages.
+// walks the KV blocks 0 .. (its last row's own block), each block's K and V
+// loaded once into LDS for all its rows, straight from global memory into the
+// second of two buffers while the first is multiplied.  Per block and tile:
+// S^T = K Q^T with 32x32x16 bf16 products, the causal cut where a row's own
+// block is reached, the online softmax (running max and sum per row,
+// accumulators rescaled), P rounded to bf16 as the B operand of
+// O^T += V^T P^T with V^T from LDS transpose reads.  The output staging tiles
+// reuse the K/V buffers after the last block.
 namespace msa {
 namespace {
 
-constexpr int kDpThreads = 256;
-constexpr int kDpRows = (kDpThreads / kWave) * 32;  // rows per workgroup
-constexpr int kDKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B)
-constexpr int kDVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B)
+constexpr int kDpThreads = 512;
+constexpr int kDpRows = (kDpThreads / kWave) * 32;  // rows per workgroup (256)
+constexpr int kDKStride = kHeadDim + 8;   // bf16 per output staging row (272 B)
 
-struct DenseShared {
-    uint16_t ks[kBlock * kDKStride];
-    uint16_t vs[kBlock * kDVStride];
+// Two K/V block buffers, loaded straight from global memory into LDS: while
+// block b is multiplied from one, block b + 1 arrives in the other.  Rows are
+// unpadded (256 B); 16-byte chunk c of K token t sits at chunk c ^ (t mod 16)
+// and of V token t at c ^ 2(t mod 8) (vs_off), which makes the K operand reads
+// and the V transpose reads conflict-free.  Each lane of a direct load writes
+// the 16 bytes at (instruction base + 16 lane), so the swizzle is chosen by
+// which global chunk a lane reads.
+struct DenseKV {
+    uint16_t k[kBlock * kHeadDim];
+    uint16_t v[kBlock * kHeadDim];
 };
-static_assert((kDpThreads / kWave) * 32 * kDKStride <= kBlock * kDKStride,
-              "query/output staging tiles fit in the K region");
+struct DenseShared {
+    DenseKV buf[2];
+};
+static_assert((kDpThreads / kWave) * 32 * kDKStride * 2 <= (int)sizeof(DenseShared),
+              "output staging fits over the K/V buffers");
+__device__ __forceinline__ int dk_off(int t, int d) {  // bf16 offset of K (token t, dim d)
+    return t * kHeadDim + ((((d >> 3) ^ (t & 15))) << 3) + (d & 7);
+}
 
-// Workgroup id -> (sequence, group, first row): sequence s has H_kv groups of
-// ceil(nq_s G / 128) row chunks each, dealt out in sequence order.  Lanes of
-// wavefront 0 scan 64 sequences at a time.  Returns false past the last one.
 __device__ bool dense_row_chunk(const int32_t* __restrict__ cu_q, int B, int Hkv, int G, int id,
                                 int* s_out, int* g_out, int* r0_out) {
     const int lane = __lane_id();
@@ -333,7 +342,7 @@ __device__ bool dense_row_chunk(const int32_t* __restrict__ cu_q, int B, int Hkv
     return false;
 }
 
-__global__ __launch_bounds__(kDpThreads, 2)
+__global__ __launch_bounds__(kDpThreads, 1)
 void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                           const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
                           const uint16_t* __restrict__ v_cache,
@@ -368,7 +377,6 @@ void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int wg_row0 = info[2];
     const int n = lane % 32;  // row of this lane within the wave's tile
     const int h = lane / 32;  // lane half
-    uint16_t* tbuf = sh.ks + wave * 32 * kDKStride;  // staging tile (aliases K)
 
     // this lane's row (rows past the sequence repeat its last row; results discarded)
     const int rho0 = wg_row0 + wave * 32 + n;
@@ -380,22 +388,38 @@ void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int last_row = min(wg_row0 + kDpRows, nrows) - 1;
     const int b_last = (L - nq + last_row / G) / kBlock;  // the workgroup's last block
 
-    // Q rows -> staging tile (coalesced 16-byte loads, 4 rows per instruction)
-    // -> B operands (k-step i of lane half h: dims 64h + 8i .. +7)
+    // K/V block -> LDS buffer: wavefront w's four direct loads per tile fill
+    // its 16-byte chunks 256w .. 256w + 255 (tokens 16w .. 16w + 15); lane l
+    // of load j fills chunk position l % 16 of token (256w + 64j + l) / 16 and
+    // so reads that token's global chunk (l % 16) ^ swizzle
+    const int32_t* bt = block_table + (size_t)s * maxblk;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto load_block = [&](int page, DenseKV& dst) {
+        const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+        const uint16_t* kp = k_cache + page_off;
+        const uint16_t* vp = v_cache + page_off;
+#pragma unroll
+        for (int jl = 0; jl < 4; ++jl) {
+            const int chunk0 = (wv * 4 + jl) * kWave;  // first 16-byte chunk of this load
+            const int tok = (chunk0 + lane) / 16, pos = lane % 16;
+            __builtin_amdgcn_global_load_lds(
+                kp + tok * kHeadDim + 8 * (pos ^ (tok & 15)),
+                (__attribute__((address_space(3))) void*)(dst.k + chunk0 * 8), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                vp + tok * kHeadDim + 8 * (pos ^ ((tok & 7) << 1)),
+                (__attribute__((address_space(3))) void*)(dst.v + chunk0 * 8), 16, 0, 0);
+        }
+    };
+    load_block(bt[0], sh.buf[0]);
+    int next_page = (b_last >= 1) ? bt[1] : 0;
+
+    // Q: B operands straight from the row (k-step i of lane half h: dims
+    // 64h + 8i .. +7)
     bf16x8 qb[8];
     {
-        const int qrow = t * Hq + head;
+        const uint16_t* qrow = q + ((size_t)t * Hq + head) * kHeadDim + 64 * h;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = lane / 16 + 4 * it;
-            const size_t off = (size_t)__shfl(qrow, r, kWave) * kHeadDim;
-            *reinterpret_cast<u32x4*>(tbuf + r * kDKStride + 8 * (lane % 16)) =
-                ld16(q + off + 8 * (lane % 16));
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            qb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(tbuf + n * kDKStride + 64 * h + 8 * i));
+        for (int i = 0; i < 8; ++i) qb[i] = as_bf16x8(ld16(qrow + 8 * i));
     }
 
     float m_run = -__builtin_inff();  // running max of this lane's row, scaled log2 units
@@ -406,42 +430,36 @@ void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int j = lane % 16;
 
     for (int b = 0; b <= b_last; ++b) {
-        __syncthreads();  // previous block's reads (and the query staging) are done
-        {
-            const int nv = min(kBlock, L - b * kBlock);
-            const int page = block_table[(size_t)s * maxblk + b];
-            const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
-            const uint16_t* kp = k_cache + page_off;
-            const uint16_t* vp = v_cache + page_off;
-            constexpr int kIt = kBlock * kHeadDim / 8 / kDpThreads;
-            u32x4 kv[kIt], vv[kIt];
-#pragma unroll
-            for (int it = 0; it < kIt; ++it) {
-                const int c = tid + kDpThreads * it;
-                const int tok = c / 16, d0 = (c % 16) * 8;
-                kv[it] = (tok < nv) ? ld16(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-                vv[it] = (tok < nv) ? ld16(vp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int it = 0; it < kIt; ++it) {
-                const int c = tid + kDpThreads * it;
-                const int tok = c / 16, d0 = (c % 16) * 8;
-                *reinterpret_cast<u32x4*>(sh.ks + tok * kDKStride + d0) = kv[it];
-                *reinterpret_cast<u32x4*>(sh.vs + tok * kDVStride + d0) = vv[it];
-            }
+        DenseKV& cur = sh.buf[b & 1];
+        // s_waitcnt immediate: vector-memory count 0, other counters free
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's loads of block b are in LDS ...
+        __syncthreads();  // ... and every wavefront's; block b - 1's buffer is free
+        const int nv = min(kBlock, L - b * kBlock);
+        if (nv < kBlock) {  // uniform: the sequence's partial last block
+            // V rows past the cache's tokens -> 0, so that P = 0 there never
+            // meets a non-finite value (K rows there are masked: they are past
+            // every row's position)
+            for (int c = tid; c < (kBlock - nv) * (kHeadDim / 8); c += kDpThreads)
+                *reinterpret_cast<u32x4*>(cur.v + (nv + c / 16) * kHeadDim + 8 * (c % 16)) =
+                    u32x4{0u, 0u, 0u, 0u};
+            __syncthreads();
         }
-        __syncthreads();
+        if (b < b_last) {  // uniform: block b + 1 arrives while block b is multiplied
+            load_block(next_page, sh.buf[(b + 1) & 1]);
+            next_page = (b + 2 <= b_last) ? bt[b + 2] : 0;
+        }
 
         // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
         // token 32mt + 8(v/4) + 4h + v%4 of row n
         f32x16 sacc[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const uint16_t* krow = sh.ks + (32 * mt + n) * kDKStride + 64 * h;
             sacc[mt] = f32x16{};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                sacc[mt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * i)), qb[i], sacc[mt]);
+                sacc[mt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(
+                                      cur.k + dk_off(32 * mt + n, 64 * h + 8 * i))),
+                                  qb[i], sacc[mt]);
         }
         // causal cut: token b*128 + tk visible iff <= p (all of a block before
         // the row's own block is visible)
@@ -489,23 +507,28 @@ void dense_prefill_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 
         // O^T = alpha O^T + V^T P^T; dim tile mt: the A operand is the same
         // tokens of dims 32mt + n from transpose reads of row-major V
-        const uint16_t* vsrc = sh.vs + (4 * h + j / 4) * kDVStride + 16 * ((lane / 16) % 2) + 4 * (j % 4);
+        // (tokens 16i + 4h + j/4 and 8 later, dims 32mt + 16((lane/16) % 2) +
+        // 4(j % 4): 4 dims of one 16-byte chunk, swizzled by token as vs_off)
+        const int vt = 4 * h + j / 4;
+        const int vd = 16 * ((lane / 16) % 2) + 4 * (j % 4);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x16 acc = o_run[mt] * alpha;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const u32x2 a0 = lds_read_tr16(vsrc + 16 * i * kDVStride + 32 * mt);
-                const u32x2 a1 = lds_read_tr16(vsrc + (16 * i + 8) * kDVStride + 32 * mt);
+                const u32x2 a0 = lds_read_tr16(cur.v + vs_off(16 * i + vt, 32 * mt + vd));
+                const u32x2 a1 = lds_read_tr16(cur.v + vs_off(16 * i + 8 + vt, 32 * mt + vd));
                 acc = mfma32(as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb[i], acc);
             }
             o_run[mt] = acc;
         }
     }
 
-    // normalised output: O^T fragments -> staging tile (row n) -> coalesced
-    // 16-byte stores of 4 rows x 256 bytes per instruction
+    // normalised output: O^T fragments -> staging tile (row n, padded rows,
+    // over the K/V buffers) -> coalesced 16-byte stores of 4 rows x 256 bytes
+    // per instruction
     __syncthreads();  // every wave is done with the last block's K/V
+    uint16_t* tbuf = reinterpret_cast<uint16_t*>(&sh) + wave * 32 * kDKStride;
     const float inv = 1.0f / l_run;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
