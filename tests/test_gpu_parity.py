@@ -45,6 +45,53 @@ SMALL = [
 ]
 
 
+def _random_config(seed: int) -> "gen.MsaConfig":
+    """A seeded random shape: batch size, GQA ratio, index heads, ragged
+    lengths (sometimes a multiple of 128, sometimes 1) and, for odd seeds,
+    several new tokens per sequence (prefill or mixed), even seeds decode."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    b = int(rng.integers(1, 7))
+    lens = []
+    for _ in range(b):
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            lens.append(int(128 * rng.integers(1, 40)))
+        elif kind == 1:
+            lens.append(int(rng.integers(1, 130)))
+        else:
+            lens.append(int(rng.integers(130, 6000)))
+    if seed % 2 == 0:
+        n_new = [1] * b
+    else:
+        n_new = [int(rng.integers(0, min(L, 200) + 1)) for L in lens]
+        if sum(n_new) == 0:
+            n_new[0] = 1
+    hidx = hkv if rng.integers(0, 3) == 0 else 1
+    return gen.MsaConfig(f"random_{seed}", lens, n_new, g * hkv, hkv, num_idx_heads=hidx,
+                         permute_pages=bool(rng.integers(0, 2)), extra_pages=int(rng.integers(0, 4)),
+                         seed=2000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_against_the_oracle(seed):
+    """Seeded random shapes (see _random_config), poisoned padding: scores,
+    selection, page table and attention against the oracle; decode shapes
+    also through the fused step (equal to the four calls)."""
+    cfg = _random_config(seed)
+    print(f"[random] {cfg.name}: lens={cfg.seq_lens} n_new={cfg.n_new} "
+          f"Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} Hidx={cfg.num_idx_heads}", flush=True)
+    x, step = parity.full_check(cfg, poison=True)
+    if cfg.is_decode:
+        fused = MsaStep(x, fused=True)
+        fused.run()
+        torch.cuda.synchronize()
+        assert torch.equal(fused.sel, step.sel)
+        assert torch.equal(fused.out, step.out)
+        assert torch.equal(fused.lse, step.lse)
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_cases_poisoned_padding(cfg):
     parity.full_check(cfg, poison=True)
