@@ -169,6 +169,29 @@ def topk_vs_torch(steps_, n):
             "msa_topk_blocks_us": round(ours * 1e3, 2), "torch_topk_us": round(theirs * 1e3, 2)}
 
 
+def append_line(cfg, xs, n):
+    """msa_append_kv (the new tokens' K, V and index keys into their pages) on
+    each layer's caches, back-to-back calls: µs per call and the bytes it
+    moves (each row read once and written once)."""
+    import torch
+    from block_sparse_attention_03_amd import _lib
+    g = torch.Generator(device="cuda").manual_seed(5)
+    T = cfg.total_q
+
+    def rows(h, dim):
+        return torch.randn((T, h, dim), generator=g, device="cuda").to(torch.bfloat16)
+
+    calls = [_lib.prepare_msa_append_kv(_lib.dims_for(cfg), T, rows(cfg.num_kv_heads, cfg.head_dim),
+                                        rows(cfg.num_kv_heads, cfg.head_dim),
+                                        rows(cfg.num_idx_heads, cfg.idx_dim), x.block_table,
+                                        x.seq_lens, x.cu_q, x.k_cache, x.v_cache, x.kidx_cache)
+             for x in xs]
+    ms = time_calls(calls, n, 4)
+    nbytes = 2 * T * (2 * cfg.num_kv_heads * cfg.head_dim + cfg.num_idx_heads * cfg.idx_dim) * 2
+    return {"us": round(ms * 1e3, 2), "bytes_moved": nbytes,
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def time_graph(steps_, steps, warmup):
     """Mean ms per layer-step when the layer-steps of all layers are captured as
     one HIP graph and the graph is replayed back to back."""
@@ -409,6 +432,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds)
+    # the step before the path: this batch's tokens into the caches (random
+    # rows; measured after everything that reads these caches)
+    append_lines = {cfg.name: append_line(cfg, layers, args.steps)}
     del fused, four, layers
     torch.cuda.empty_cache()
     ceil = measured_ceilings()
@@ -518,6 +544,8 @@ def main():
         del dfn
         topk_line[c3.name] = topk_vs_torch(s3, n3)
         also["topk_vs_torch"] = topk_line
+        append_lines[c3.name] = append_line(c3, l3, n3)
+        also["cache_append"] = append_lines
         also["dense_gqa_decode"] = dense
         del s3, l3
         torch.cuda.empty_cache()

@@ -29,7 +29,7 @@ EXPORTED = (
     "msa_sparse_attn_prefill", "msa_decode_workspace_size", "msa_prefill_workspace_size",
     "msa_status_string", "msa_abi_version", "msa_decode_step", "msa_decode_step_workspace_size",
     "msa_dense_attn_decode", "msa_dense_decode_workspace_size", "msa_dense_attn_prefill",
-    "msa_validate_inputs",
+    "msa_validate_inputs", "msa_append_kv",
 )
 
 
@@ -79,11 +79,13 @@ def lib():
         L.msa_dense_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
         L.msa_dense_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P]
         L.msa_validate_inputs.argtypes = [D, I32, P, P, P, P, P]
+        L.msa_append_kv.argtypes = [D, I32, P, P, P, P, P, P, P, P, P, P]
         L.msa_dense_decode_workspace_size.argtypes = [D]
         L.msa_dense_decode_workspace_size.restype = SZ
         for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
                   "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_decode_step",
-                  "msa_dense_attn_decode", "msa_dense_attn_prefill", "msa_validate_inputs"):
+                  "msa_dense_attn_decode", "msa_dense_attn_prefill", "msa_validate_inputs",
+                  "msa_append_kv"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_decode_workspace_size.argtypes = [D]
         L.msa_decode_workspace_size.restype = SZ
@@ -367,6 +369,33 @@ def msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_
     """Dense causal attention over every cached token (the prefill baseline)."""
     prepare_msa_dense_attn_prefill(dims, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
                                    out, lse)(stream)
+
+
+def prepare_msa_append_kv(dims, total_q, k_new, v_new, kidx_new, block_table, seq_lens, cu_q,
+                          k_cache, v_cache, kidx_cache):
+    """msa_append_kv with its arguments checked and packed once: returns a
+    PreparedCall that repeats the call, on the current (or a given) stream."""
+    d = dims
+    B, H = d.num_seqs, d.num_kv_heads
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    icache = (d.num_pages, d.num_idx_heads, d.block_size, d.idx_dim)
+    args = (_ptr(k_new, BF16, "k_new", (total_q, H, d.head_dim)),
+            _ptr(v_new, BF16, "v_new", (total_q, H, d.head_dim)),
+            _ptr(kidx_new, BF16, "kidx_new", (total_q, d.num_idx_heads, d.idx_dim)),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
+            _ptr(k_cache, BF16, "k_cache", cache), _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(kidx_cache, BF16, "kidx_cache", icache))
+    return PreparedCall(lib().msa_append_kv, (ctypes.byref(d), total_q, *args), "msa_append_kv",
+                        (d, k_new, v_new, kidx_new, block_table, seq_lens, cu_q, k_cache,
+                         v_cache, kidx_cache))
+
+
+def msa_append_kv(dims, total_q, k_new, v_new, kidx_new, block_table, seq_lens, cu_q, k_cache,
+                  v_cache, kidx_cache, stream=None):
+    """The new tokens' K, V and index keys into their pages (include/msa.h)."""
+    prepare_msa_append_kv(dims, total_q, k_new, v_new, kidx_new, block_table, seq_lens, cu_q,
+                          k_cache, v_cache, kidx_cache)(stream)
 
 
 MSA_FAULT_SEQ_LEN, MSA_FAULT_CU_Q, MSA_FAULT_BLOCK_TABLE = 1, 2, 4

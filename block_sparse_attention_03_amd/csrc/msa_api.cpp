@@ -241,6 +241,28 @@ msa_status_t msa_dense_attn_prefill(const msa_dims_t* dims, int32_t total_q, con
                                              cu_q, out, lse, static_cast<hipStream_t>(stream)));
 }
 
+msa_status_t msa_append_kv(const msa_dims_t* dims, int32_t total_q, const uint16_t* k_new,
+                           const uint16_t* v_new, const uint16_t* kidx_new,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* cu_q, uint16_t* k_cache, uint16_t* v_cache,
+                           uint16_t* kidx_cache, void* stream) {
+    MsaShape s;
+    msa_status_t st = check_dims(dims, &s);
+    if (st != MSA_SUCCESS) return st;
+    if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
+    if (!k_new || !v_new || !kidx_new || !block_table || !seq_lens || !cu_q || !k_cache ||
+        !v_cache || !kidx_cache)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kidx_new, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(cu_q, 4) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(kidx_cache, 16))
+        return MSA_ERROR_INVALID_VALUE;
+    return launched(msa_launch_append_kv(s, total_q, k_new, v_new, kidx_new, block_table, seq_lens,
+                                         cu_q, k_cache, v_cache, kidx_cache,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 msa_status_t msa_validate_inputs(const msa_dims_t* dims, int32_t total_q, const int32_t* block_table,
                                  const int32_t* seq_lens, const int32_t* cu_q, int32_t* status,
                                  void* stream) {

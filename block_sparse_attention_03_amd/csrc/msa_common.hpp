@@ -126,6 +126,11 @@ struct MsaShape {
     float scale;  // resolved softmax scale (> 0)
 };
 
+hipError_t msa_launch_append_kv(const MsaShape& s, int total_q, const uint16_t* k_new,
+                                const uint16_t* v_new, const uint16_t* kidx_new,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* cu_q, uint16_t* k_cache, uint16_t* v_cache,
+                                uint16_t* kidx_cache, hipStream_t st);
 hipError_t msa_launch_validate(const MsaShape& s, int total_q, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* cu_q, int32_t* status,
                                hipStream_t st);

@@ -49,6 +49,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 struct SeqInfo {
     int q0, nq, L;  // first query token, query count and cache length of the sequence
+    int s;          // the sequence
 };
 
 // Sequence of the wave-uniform query token t.  Lanes read cu_q / seq_lens of
@@ -69,6 +70,7 @@ __device__ __forceinline__ SeqInfo lookup_seq(const int32_t* __restrict__ cu_q,
             r.q0 = __shfl(c0, cnt, kWave);
             r.nq = __shfl(c1, cnt, kWave) - r.q0;
             r.L = __shfl(L, cnt, kWave);
+            r.s = base + cnt;
             return r;
         }
     }

@@ -232,6 +232,25 @@ msa_status_t msa_dense_attn_prefill(const msa_dims_t *dims, int32_t total_q, con
                                     const int32_t *cu_q, uint16_t *out, float *lse, void *stream);
 
 /*
+ * Cache append, the step before scoring ([aivizor] paragraph on MSA with paged
+ * attention: the caches are paged by 128-token blocks): the i-th new token of
+ * sequence s (query token t = cu_q[s] + i) sits at position
+ * p = seq_lens[s] - n_s + i, i.e. page block_table[s][p / Bk], slot p % Bk,
+ * and its rows are copied there -- the (cu_q, seq_lens) convention of
+ * msa_sparse_attn_prefill, so decode is cu_q[s] = s.
+ *   k_new, v_new [total_q, H_kv, 128] bf16; kidx_new [total_q, H_idx, 64] bf16
+ *   k_cache, v_cache [num_pages, H_kv, 128, 128], kidx_cache
+ *   [num_pages, H_idx, 128, 64] (updated in place: only the new tokens' slots
+ *   are written)
+ * The new tokens' slots must be distinct (no two tokens at one position).
+ */
+msa_status_t msa_append_kv(const msa_dims_t *dims, int32_t total_q, const uint16_t *k_new,
+                           const uint16_t *v_new, const uint16_t *kidx_new,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           const int32_t *cu_q, uint16_t *k_cache, uint16_t *v_cache,
+                           uint16_t *kidx_cache, void *stream);
+
+/*
  * Device-side check of the content preconditions listed at the top of this
  * file, for callers that want them verified (not a hot-path call): for every
  * sequence s, 1 <= seq_lens[s] <= max_blocks_per_seq*Bk; with cu_q,

@@ -88,6 +88,25 @@ def positions(seq_lens, cu_q):
     return seq_of[:T], pos_of[:T]
 
 
+def append_kv(k_cache, v_cache, kidx_cache, k_new, v_new, kidx_new, block_table, seq_lens,
+              cu_q, block_size):
+    """Cache append by its definition ([aivizor] paragraph on MSA with paged
+    attention: paged caches, one page per block): the i-th new token of
+    sequence s, at position p = seq_lens[s] - n_s + i, goes to page
+    block_table[s][p // block_size], slot p % block_size, for every KV group
+    (K, V) and index head (k_idx).  Works on raw bf16 bits; returns updated
+    copies of the three caches."""
+    seq_of, pos_of = positions(seq_lens, cu_q)
+    K, V, I = k_cache.copy(), v_cache.copy(), kidx_cache.copy()
+    for t in range(len(seq_of)):
+        s, p = int(seq_of[t]), int(pos_of[t])
+        page = int(block_table[s][p // block_size])
+        K[page, :, p % block_size, :] = k_new[t]
+        V[page, :, p % block_size, :] = v_new[t]
+        I[page, :, p % block_size, :] = kidx_new[t]
+    return K, V, I
+
+
 def index_score(q_idx, kidx_cache, block_table, seq_of, pos_of, block_size, rows=None):
     """fp64 block scores [n_rows, maxblk] (rows: flat t*H_kv+g, default all)."""
     q_idx = _c(q_idx, np.uint16)

@@ -390,6 +390,72 @@ def test_fused_decode_step_rows_past_8192_blocks():
         assert torch.equal(fused.lse, ref.lse)
 
 
+def _new_rows(cfg, x, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    T = cfg.total_q
+    k_new = torch.randn((T, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    v_new = torch.randn((T, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    i_new = torch.randn((T, cfg.num_idx_heads, cfg.idx_dim), generator=g, device="cuda").to(torch.bfloat16)
+    return k_new, v_new, i_new
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[6], SMALL[7],
+                                 SMALL[1].with_idx_heads(SMALL[1].num_kv_heads)],
+                         ids=lambda c: f"{c.name}_hidx{c.num_idx_heads}")
+def test_append_kv_matches_the_oracle(cfg):
+    """msa_append_kv writes each new token's K, V and index-key rows into its
+    page slot and nothing else: the three caches equal the oracle's, bit for
+    bit (decode, a mixed batch with a sequence of no new tokens, multi-query
+    decode, per-group index keys)."""
+    import oracle
+    print(f"[append] {cfg.name} Hidx={cfg.num_idx_heads}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda")
+    k_new, v_new, i_new = _new_rows(cfg, x, 70)
+    before = [gen.bits(t) for t in (x.k_cache, x.v_cache, x.kidx_cache)]
+    L.msa_append_kv(L.dims_for(cfg), cfg.total_q, k_new, v_new, i_new, x.block_table, x.seq_lens,
+                    x.cu_q, x.k_cache, x.v_cache, x.kidx_cache)
+    torch.cuda.synchronize()
+    ref = oracle.append_kv(*before, gen.bits(k_new), gen.bits(v_new), gen.bits(i_new),
+                           gen.bits(x.block_table), gen.bits(x.seq_lens), gen.bits(x.cu_q),
+                           cfg.block_size)
+    for name, got, want in zip(("k_cache", "v_cache", "kidx_cache"),
+                               (x.k_cache, x.v_cache, x.kidx_cache), ref):
+        assert np.array_equal(gen.bits(got), want), name
+
+
+def test_append_then_decode_step_equals_the_full_cache():
+    """The decode step after appending the current tokens (their slots
+    poisoned first) equals the step on the cache that already held them."""
+    import oracle
+    cfg = gen.MsaConfig("append_step", [9000, 3000, 700, 128], [1] * 4, 12, 3, permute_pages=True,
+                        seed=66)
+    print(f"[append-step] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda")
+    ref = MsaStep(x, fused=True)
+    ref.run()
+    torch.cuda.synchronize()
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    bt = gen.bits(x.block_table)
+    pages = torch.tensor([int(bt[s][p // cfg.block_size]) for s, p in zip(seq_of, pos_of)],
+                         device="cuda", dtype=torch.long)
+    slots = torch.tensor([int(p % cfg.block_size) for p in pos_of], device="cuda", dtype=torch.long)
+    k_new = x.k_cache[pages, :, slots, :].clone()
+    v_new = x.v_cache[pages, :, slots, :].clone()
+    i_new = x.kidx_cache[pages, :, slots, :].clone()
+    nan = float("nan")
+    x.k_cache[pages, :, slots, :] = nan
+    x.v_cache[pages, :, slots, :] = nan
+    x.kidx_cache[pages, :, slots, :] = nan
+    L.msa_append_kv(L.dims_for(cfg), cfg.total_q, k_new, v_new, i_new, x.block_table, x.seq_lens,
+                    x.cu_q, x.k_cache, x.v_cache, x.kidx_cache)
+    step = MsaStep(x, fused=True)
+    step.run()
+    torch.cuda.synchronize()
+    assert torch.equal(step.sel, ref.sel)
+    assert torch.equal(step.out, ref.out)
+    assert torch.equal(step.lse, ref.lse)
+
+
 def _dense_decode(cfg, x):
     d = L.dims_for(cfg)
     ws = torch.empty(L.msa_dense_decode_workspace_size(d), dtype=torch.uint8, device="cuda")

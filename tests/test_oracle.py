@@ -426,3 +426,34 @@ def test_self_check_budget_invariant():
     n_att = np.exp(l)
     assert (np.round(n_att) <= cfg.topk * Bk).all()
     assert np.allclose(n_att, np.round(n_att), atol=1e-8)
+
+
+def test_append_kv_hand_example():
+    """Cache append: sequence 0 (5 tokens, 2 new at positions 3 and 4),
+    sequence 1 (3 tokens, 1 new at position 2), pages of 4 tokens.  Token 0
+    -> page 7 slot 3, token 1 -> page 2 slot 0, token 2 -> page 5 slot 2;
+    nothing else changes."""
+    import oracle
+    rng = np.random.default_rng(7)
+    P, H, Hi, Bk, D, d = 8, 2, 1, 4, 3, 2
+    k = rng.integers(0, 1 << 16, size=(P, H, Bk, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(P, H, Bk, D), dtype=np.uint16)
+    ki = rng.integers(0, 1 << 16, size=(P, Hi, Bk, d), dtype=np.uint16)
+    kn = rng.integers(0, 1 << 16, size=(3, H, D), dtype=np.uint16)
+    vn = rng.integers(0, 1 << 16, size=(3, H, D), dtype=np.uint16)
+    kin = rng.integers(0, 1 << 16, size=(3, Hi, d), dtype=np.uint16)
+    bt = np.array([[7, 2], [5, 0]], np.int32)
+    K, V, I = oracle.append_kv(k, v, ki, kn, vn, kin, bt, np.array([5, 3], np.int32),
+                               np.array([0, 2, 3], np.int32), Bk)
+    where = {(7, 3): 0, (2, 0): 1, (5, 2): 2}
+    for page in range(P):
+        for slot in range(Bk):
+            t = where.get((page, slot))
+            if t is None:
+                assert (K[page, :, slot] == k[page, :, slot]).all()
+                assert (V[page, :, slot] == v[page, :, slot]).all()
+                assert (I[page, :, slot] == ki[page, :, slot]).all()
+            else:
+                assert (K[page, :, slot] == kn[t]).all()
+                assert (V[page, :, slot] == vn[t]).all()
+                assert (I[page, :, slot] == kin[t]).all()
