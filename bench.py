@@ -169,10 +169,13 @@ def topk_vs_torch(steps_, n):
             "msa_topk_blocks_us": round(ours * 1e3, 2), "torch_topk_us": round(theirs * 1e3, 2)}
 
 
-def append_line(cfg, xs, n):
+def append_line(cfg, xs, n, steps_=None):
     """msa_append_kv (the new tokens' K, V and index keys into their pages) on
     each layer's caches, back-to-back calls: µs per call and the bytes it
-    moves (each row read once and written once)."""
+    moves (each row read once and written once).  With the layers' fused decode
+    steps (decode only), also the serving-loop pair -- msa_append_kv then
+    msa_decode_step -- against msa_decode_step_append, which appends inside
+    the step's scoring launch: µs per layer-step."""
     import torch
     from block_sparse_attention_03_amd import _lib
     g = torch.Generator(device="cuda").manual_seed(5)
@@ -181,15 +184,27 @@ def append_line(cfg, xs, n):
     def rows(h, dim):
         return torch.randn((T, h, dim), generator=g, device="cuda").to(torch.bfloat16)
 
-    calls = [_lib.prepare_msa_append_kv(_lib.dims_for(cfg), T, rows(cfg.num_kv_heads, cfg.head_dim),
-                                        rows(cfg.num_kv_heads, cfg.head_dim),
-                                        rows(cfg.num_idx_heads, cfg.idx_dim), x.block_table,
-                                        x.seq_lens, x.cu_q, x.k_cache, x.v_cache, x.kidx_cache)
-             for x in xs]
+    new = [(rows(cfg.num_kv_heads, cfg.head_dim), rows(cfg.num_kv_heads, cfg.head_dim),
+            rows(cfg.num_idx_heads, cfg.idx_dim)) for _ in xs]
+    calls = [_lib.prepare_msa_append_kv(_lib.dims_for(cfg), T, k, v, i, x.block_table, x.seq_lens,
+                                        x.cu_q, x.k_cache, x.v_cache, x.kidx_cache)
+             for x, (k, v, i) in zip(xs, new)]
     ms = time_calls(calls, n, 4)
     nbytes = 2 * T * (2 * cfg.num_kv_heads * cfg.head_dim + cfg.num_idx_heads * cfg.idx_dim) * 2
-    return {"us": round(ms * 1e3, 2), "bytes_moved": nbytes,
+    line = {"us": round(ms * 1e3, 2), "bytes_moved": nbytes,
             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    if steps_ is not None and cfg.is_decode:
+        pairs = []
+        for c, st in zip(calls, steps_):
+            pairs += [c, st.fused_step]
+        line["append_then_step_us"] = round(time_calls(pairs, 2 * n, 8) * 2e3, 2)
+        joint = [_lib.prepare_msa_decode_step_append(
+                     st.dims, k, v, i, st.x.q_idx, st.x.kidx_cache, st.x.q, st.x.k_cache,
+                     st.x.v_cache, st.x.block_table, st.x.seq_lens, st.out, st.lse, st.sel,
+                     st.workspace)
+                 for st, (k, v, i) in zip(steps_, new)]
+        line["step_append_us"] = round(time_calls(joint, n, 4) * 1e3, 2)
+    return line
 
 
 def time_graph(steps_, steps, warmup):
@@ -434,7 +449,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds)
     # the step before the path: this batch's tokens into the caches (random
     # rows; measured after everything that reads these caches)
-    append_lines = {cfg.name: append_line(cfg, layers, args.steps)}
+    append_lines = {cfg.name: append_line(cfg, layers, args.steps, fused)}
     del fused, four, layers
     torch.cuda.empty_cache()
     ceil = measured_ceilings()

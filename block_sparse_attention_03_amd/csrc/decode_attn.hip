@@ -357,7 +357,8 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
                                   const uint16_t* q, const uint16_t* k_cache,
                                   const uint16_t* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, uint16_t* out, float* lse,
-                                  int32_t* sel_out, void* ws, hipStream_t st) {
+                                  int32_t* sel_out, void* ws, const DecodeAppend* app,
+                                  hipStream_t st) {
     using namespace msa;
     const int R = s.B * s.Hkv;
     if (R == 0) return hipSuccess;
@@ -365,7 +366,7 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
     float* scores = reinterpret_cast<float*>(base + msa_decode_ws_bytes(s));
     int32_t* row_lens = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(scores) +
                                                    align256((size_t)R * s.maxblk * sizeof(float)));
-    hipError_t e = msa_launch_index_score_decode(s, q_idx, kidx, block_table, seq_lens, scores, st);
+    hipError_t e = msa_launch_index_score_decode(s, q_idx, kidx, block_table, seq_lens, scores, app, st);
     if (e != hipSuccess) return e;
     const int m = s.maxblk;
     if (m > kFusedMaxBlocks) {

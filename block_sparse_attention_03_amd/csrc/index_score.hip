@@ -35,18 +35,33 @@ namespace {
 
 constexpr int kScoreWaves = 4;  // blocks per workgroup (one per wavefront)
 
+// The new decode tokens' rows, for the step that appends them to the caches
+// as it scores (one token per sequence, at position seq_lens[s] - 1).
+struct AppendRows {
+    const uint16_t* kidx_new;  // [B, Hidx, 64]
+    const uint16_t* k_new;     // [B, Hkv, 128]
+    const uint16_t* v_new;     // [B, Hkv, 128]
+    uint16_t* kidx_cache;      // [P, Hidx, 128, 64], the array scored
+    uint16_t* k_cache;         // [P, Hkv, 128, 128]
+    uint16_t* v_cache;
+};
+
 // kInvisible: write -inf for the blocks past every row's position (the ABI's
 // score rows); the fused decode step, whose selection never reads them,
-// skips those stores.
-template <bool kInvisible>
+// skips those stores.  kAppend (decode only): the wavefront of each
+// sequence's last block writes the new token's rows into the caches and
+// scores its index-key row from the new values, so the cache slot is never
+// read back in this launch; the attention launches that follow see the
+// appended K/V.
+template <bool kInvisible, bool kAppend>
 __global__ __launch_bounds__(kScoreWaves * kWave)
 void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
-                        const uint16_t* __restrict__ kidx,    // [P, Hidx, 128, 64]
+                        const uint16_t* kidx,                 // [P, Hidx, 128, 64]
                         const int32_t* __restrict__ block_table,
                         const int32_t* __restrict__ seq_lens,
                         const int32_t* __restrict__ cu_q,
                         float* __restrict__ scores,           // [T, Hkv, maxblk]
-                        int Hkv, int Hidx, int maxblk) {
+                        int Hkv, int Hidx, int maxblk, AppendRows ap) {
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int b = blockIdx.x * kScoreWaves + wave;
@@ -102,6 +117,13 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     u32x4 raw[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) raw[j] = ld16_stream(kb + kWave * j + lane);
+    // kAppend: this wavefront's block holds the sequence's new token (decode:
+    // position L - 1) in slot tn; lanes 0..7 fetch its 8 index-key pieces.
+    const bool new_block = kAppend && b == last_pos / kBlock;  // wave-uniform
+    const int tn = last_pos % kBlock;
+    u32x4 knew = {0u, 0u, 0u, 0u};
+    if (new_block && lane < 8)
+        knew = ld16(ap.kidx_new + ((size_t)s * Hidx + ih) * kIdxDim + 8 * lane);
     bf16x8 a[8][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -109,6 +131,13 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
         for (int jj = 0; jj < 8; ++jj) {
             const int t = 8 * jj + lane / 8;  // local token (tokens 64 half + t)
             st[t * 8 + ((lane % 8) ^ (t & 7))] = raw[8 * half + jj];
+        }
+        if (new_block && tn / 64 == half && lane < 8) {
+            // the slot's row comes from the new keys (this later LDS write of
+            // the same wavefront lands after the stale one) and goes to the cache
+            st[(tn % 64) * 8 + (lane ^ (tn & 7))] = knew;
+            *reinterpret_cast<u32x4*>(ap.kidx_cache + (((size_t)page * Hidx + ih) * kBlock + tn) * kIdxDim +
+                                      8 * lane) = knew;
         }
 #pragma unroll
         for (int mq = 0; mq < 4; ++mq) {
@@ -150,6 +179,20 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
         best = wave_max_xor(best, 16);
         best = wave_max_xor(best, 32);
         if (kg == 0 && row_ok) scores[((size_t)t * Hkv + g) * maxblk + b] = best;
+    }
+    if (new_block && ih == 0) {
+        // the new token's K and V rows (one per KV group), read by the
+        // attention launches that follow
+        constexpr int kPieces = kHeadDim / 8;  // 16-byte pieces per K or V row
+        for (int c = lane; c < Hkv * kPieces; c += kWave) {
+            const int g = c / kPieces;
+            const size_t src = ((size_t)s * Hkv + g) * kHeadDim + 8 * (c % kPieces);
+            const size_t dst = (((size_t)page * Hkv + g) * kBlock + tn) * kHeadDim + 8 * (c % kPieces);
+            const u32x4 kv = ld16(ap.k_new + src);
+            const u32x4 vv = ld16(ap.v_new + src);
+            *reinterpret_cast<u32x4*>(ap.k_cache + dst) = kv;
+            *reinterpret_cast<u32x4*>(ap.v_cache + dst) = vv;
+        }
     }
 }
 
@@ -410,21 +453,33 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
         return hipGetLastError();
     }
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
-    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(kScoreWaves * kWave), 0, st, q_idx, kidx,
-                       block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk);
+    hipLaunchKernelGGL((index_score_kernel<true, false>), grid, dim3(kScoreWaves * kWave), 0, st,
+                       q_idx, kidx, block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk,
+                       AppendRows{});
     return hipGetLastError();
 }
 
 hipError_t msa_launch_index_score_decode(const MsaShape& s, const uint16_t* q_idx,
                                          const uint16_t* kidx, const int32_t* block_table,
-                                         const int32_t* seq_lens, float* scores, hipStream_t st) {
+                                         const int32_t* seq_lens, float* scores,
+                                         const DecodeAppend* app, hipStream_t st) {
     using namespace msa;
     if (s.B == 0) return hipSuccess;
     // scores past each row's own block stay unwritten: the decode step's
     // selection gives blocks past b_loc no key and never reads their values
     dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
-    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(kScoreWaves * kWave), 0, st, q_idx,
-                       kidx, block_table, seq_lens, static_cast<const int32_t*>(nullptr), scores,
-                       s.Hkv, s.Hidx, s.maxblk);
+    if (app) {
+        const AppendRows ap{app->kidx_new, app->k_new, app->v_new,
+                            app->kidx_cache, app->k_cache, app->v_cache};
+        hipLaunchKernelGGL((index_score_kernel<false, true>), grid, dim3(kScoreWaves * kWave), 0,
+                           st, q_idx, static_cast<const uint16_t*>(app->kidx_cache), block_table,
+                           seq_lens, static_cast<const int32_t*>(nullptr), scores, s.Hkv, s.Hidx,
+                           s.maxblk, ap);
+    } else {
+        hipLaunchKernelGGL((index_score_kernel<false, false>), grid, dim3(kScoreWaves * kWave), 0,
+                           st, q_idx, kidx, block_table, seq_lens,
+                           static_cast<const int32_t*>(nullptr), scores, s.Hkv, s.Hidx, s.maxblk,
+                           AppendRows{});
+    }
     return hipGetLastError();
 }

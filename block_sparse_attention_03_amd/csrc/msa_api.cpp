@@ -169,16 +169,20 @@ size_t msa_decode_step_workspace_size(const msa_dims_t* dims) {
     return msa_decode_step_ws_bytes(s);
 }
 
-msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
-                             const uint16_t* kidx_cache, const uint16_t* q,
-                             const uint16_t* k_cache, const uint16_t* v_cache,
-                             const int32_t* block_table, const int32_t* seq_lens, uint16_t* out,
-                             float* lse, int32_t* sel, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+// The decode step's checks and launches, with or without the cache append.
+static msa_status_t decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
+                                const uint16_t* kidx_cache, const uint16_t* q,
+                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                uint16_t* out, float* lse, int32_t* sel, void* workspace,
+                                size_t workspace_bytes, const DecodeAppend* app, void* stream) {
     MsaShape s;
     msa_status_t st = check_dims(dims, &s);
     if (st != MSA_SUCCESS) return st;
     if (s.B == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
+    if (app && (!app->k_new || !app->v_new || !app->kidx_new || !aligned(app->k_new, 16) ||
+                !aligned(app->v_new, 16) || !aligned(app->kidx_new, 16)))
+        return MSA_ERROR_INVALID_VALUE;
     if (!q_idx || !kidx_cache || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return MSA_ERROR_INVALID_VALUE;
     if (!aligned(q_idx, 16) || !aligned(kidx_cache, 16) || !aligned(q, 16) ||
@@ -190,8 +194,30 @@ msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < msa_decode_step_ws_bytes(s))
         return MSA_ERROR_WORKSPACE;
     return launched(msa_launch_decode_step(s, q_idx, kidx_cache, q, k_cache, v_cache, block_table,
-                                           seq_lens, out, lse, sel, workspace,
+                                           seq_lens, out, lse, sel, workspace, app,
                                            static_cast<hipStream_t>(stream)));
+}
+
+msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
+                             const uint16_t* kidx_cache, const uint16_t* q,
+                             const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, uint16_t* out,
+                             float* lse, int32_t* sel, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
+                       lse, sel, workspace, workspace_bytes, nullptr, stream);
+}
+
+msa_status_t msa_decode_step_append(const msa_dims_t* dims, const uint16_t* k_new,
+                                    const uint16_t* v_new, const uint16_t* kidx_new,
+                                    const uint16_t* q_idx, uint16_t* kidx_cache,
+                                    const uint16_t* q, uint16_t* k_cache, uint16_t* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    uint16_t* out, float* lse, int32_t* sel, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const DecodeAppend app{k_new, v_new, kidx_new, k_cache, v_cache, kidx_cache};
+    return decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
+                       lse, sel, workspace, workspace_bytes, &app, stream);
 }
 
 size_t msa_dense_decode_workspace_size(const msa_dims_t* dims) {

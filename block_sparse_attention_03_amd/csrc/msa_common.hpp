@@ -155,9 +155,20 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                               const int32_t* block_table, const int32_t* seq_lens,
                               const int32_t* cu_q, const int32_t* sel, uint16_t* out, float* lse,
                               void* ws, hipStream_t st);
+// The new decode tokens (one per sequence) that a decode step writes into the
+// caches while it scores.
+struct DecodeAppend {
+    const uint16_t* k_new;     // [B, Hkv, 128]
+    const uint16_t* v_new;     // [B, Hkv, 128]
+    const uint16_t* kidx_new;  // [B, Hidx, 64]
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    uint16_t* kidx_cache;
+};
 hipError_t msa_launch_index_score_decode(const MsaShape& s, const uint16_t* q_idx,
                                          const uint16_t* kidx, const int32_t* block_table,
-                                         const int32_t* seq_lens, float* scores, hipStream_t st);
+                                         const int32_t* seq_lens, float* scores,
+                                         const DecodeAppend* app, hipStream_t st);
 size_t msa_dense_decode_ws_bytes(const MsaShape& s);
 hipError_t msa_launch_dense_decode(const MsaShape& s, const uint16_t* q, const uint16_t* k_cache,
                                    const uint16_t* v_cache, const int32_t* block_table,
@@ -173,4 +184,5 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
                                   const uint16_t* q, const uint16_t* k_cache,
                                   const uint16_t* v_cache, const int32_t* block_table,
                                   const int32_t* seq_lens, uint16_t* out, float* lse,
-                                  int32_t* sel_out, void* ws, hipStream_t st);
+                                  int32_t* sel_out, void* ws, const DecodeAppend* app,
+                                  hipStream_t st);

@@ -251,6 +251,28 @@ msa_status_t msa_append_kv(const msa_dims_t *dims, int32_t total_q, const uint16
                            uint16_t *kidx_cache, void *stream);
 
 /*
+ * msa_append_kv followed by msa_decode_step, in the decode step's three
+ * launches: the new token of each sequence (position seq_lens[s] - 1, so
+ * seq_lens already counts it) is written into its page slot by the scoring
+ * launch ([aivizor] paragraph on MSA with paged attention), which scores that
+ * slot from the new index keys; the selection and attention launches then
+ * read the updated caches.  Results and cache contents equal those of the two
+ * calls, bit for bit.
+ *   k_new, v_new [B, H_kv, 128] bf16; kidx_new [B, H_idx, 64] bf16
+ *   k_cache, v_cache, kidx_cache: updated in place (only the new slots)
+ *   the other arguments as msa_decode_step (same workspace size)
+ * The new slots must be distinct; k_new, v_new and kidx_new must not overlap
+ * the caches.
+ */
+msa_status_t msa_decode_step_append(const msa_dims_t *dims, const uint16_t *k_new,
+                                    const uint16_t *v_new, const uint16_t *kidx_new,
+                                    const uint16_t *q_idx, uint16_t *kidx_cache,
+                                    const uint16_t *q, uint16_t *k_cache, uint16_t *v_cache,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    uint16_t *out, float *lse, int32_t *sel, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * Device-side check of the content preconditions listed at the top of this
  * file, for callers that want them verified (not a hot-path call): for every
  * sequence s, 1 <= seq_lens[s] <= max_blocks_per_seq*Bk; with cu_q,

@@ -155,12 +155,14 @@ def test_calls_with_no_work_succeed_without_pointers():
     assert lib.msa_build_page_table(d, N, N, N, N, N, N) == ok
     assert lib.msa_sparse_attn_decode(d, N, N, N, N, N, N, N, N, 0, N) == ok
     assert lib.msa_decode_step(d, N, N, N, N, N, N, N, N, N, N, N, 0, N) == ok
+    assert lib.msa_decode_step_append(d, N, N, N, N, N, N, N, N, N, N, N, N, N, N, 0, N) == ok
     assert lib.msa_dense_attn_decode(d, N, N, N, N, N, N, N, N, 0, N) == ok
     # work to do: the NULL pointers are refused
     d = ctypes.byref(some)
     assert lib.msa_append_kv(d, 3, N, N, N, N, N, N, N, N, N, N) == L.MSA_ERROR_INVALID_VALUE
     assert lib.msa_index_score(d, 3, N, N, N, N, N, N, N) == L.MSA_ERROR_INVALID_VALUE
     assert lib.msa_decode_step(d, N, N, N, N, N, N, N, N, N, N, N, 0, N) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_decode_step_append(d, N, N, N, N, N, N, N, N, N, N, N, N, N, N, 0, N) == L.MSA_ERROR_INVALID_VALUE
     # invalid dims are still invalid with no work
     bad = dims(num_seqs=0, num_q_heads=7)
     assert lib.msa_index_score(ctypes.byref(bad), 0, N, N, N, N, N, N, N) == L.MSA_ERROR_INVALID_VALUE

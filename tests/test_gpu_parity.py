@@ -456,6 +456,58 @@ def test_append_then_decode_step_equals_the_full_cache():
     assert torch.equal(step.lse, ref.lse)
 
 
+@pytest.mark.parametrize("hidx", [1, 3])
+def test_decode_step_append_equals_append_then_step(hidx):
+    """msa_decode_step_append (the append done by the scoring launch) leaves
+    the same caches, selection, output and LSE as msa_append_kv followed by
+    msa_decode_step, bit for bit; the caches also equal the oracle's append.
+    The new slots are poisoned with NaN first, so a slot read before it is
+    written shows.  Lengths put the new token at slots 0, 59 and 127 of a
+    block, in the first and in later blocks, with one index head and with one
+    per KV group."""
+    import oracle
+    cfg = gen.MsaConfig("step_append", [9000, 3000, 700, 128, 1, 129], [1] * 6, 12, 3,
+                        permute_pages=True, seed=67).with_idx_heads(hidx)
+    print(f"[step-append] {cfg.name} Hidx={hidx}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda")
+    k_new, v_new, i_new = _new_rows(cfg, x, 71)
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    bt = gen.bits(x.block_table)
+    pages = torch.tensor([int(bt[s][p // cfg.block_size]) for s, p in zip(seq_of, pos_of)],
+                         device="cuda", dtype=torch.long)
+    slots = torch.tensor([int(p % cfg.block_size) for p in pos_of], device="cuda", dtype=torch.long)
+    for c in (x.k_cache, x.v_cache, x.kidx_cache):
+        c[pages, :, slots, :] = float("nan")
+    before = [gen.bits(t) for t in (x.k_cache, x.v_cache, x.kidx_cache)]
+    want = oracle.append_kv(*before, gen.bits(k_new), gen.bits(v_new), gen.bits(i_new),
+                            bt, cfg.seq_lens, gen.bits(x.cu_q), cfg.block_size)
+    d = L.dims_for(cfg)
+    B, Hq, H = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads
+
+    def outputs():
+        ws = torch.empty(L.msa_decode_step_workspace_size(d), dtype=torch.uint8, device="cuda")
+        return (torch.empty_like(x.q), torch.empty((B, Hq), dtype=torch.float32, device="cuda"),
+                torch.empty((B, H, cfg.topk), dtype=torch.int32, device="cuda"), ws)
+
+    caches_a = [t.clone() for t in (x.k_cache, x.v_cache, x.kidx_cache)]
+    out_a, lse_a, sel_a, ws_a = outputs()
+    L.msa_append_kv(d, B, k_new, v_new, i_new, x.block_table, x.seq_lens, x.cu_q, *caches_a)
+    L.msa_decode_step(d, x.q_idx, caches_a[2], x.q, caches_a[0], caches_a[1], x.block_table,
+                      x.seq_lens, out_a, lse_a, sel_a, ws_a)
+    out_b, lse_b, sel_b, ws_b = outputs()
+    L.msa_decode_step_append(d, k_new, v_new, i_new, x.q_idx, x.kidx_cache, x.q, x.k_cache,
+                             x.v_cache, x.block_table, x.seq_lens, out_b, lse_b, sel_b, ws_b)
+    torch.cuda.synchronize()
+    for name, got_a, got_b, ref in zip(("k", "v", "kidx"), caches_a,
+                                       (x.k_cache, x.v_cache, x.kidx_cache), want):
+        assert np.array_equal(gen.bits(got_a), ref), name
+        assert np.array_equal(gen.bits(got_b), ref), name
+    assert torch.equal(sel_b, sel_a)
+    assert torch.equal(out_b, out_a)
+    assert torch.equal(lse_b, lse_a)
+    assert torch.isfinite(lse_b).all()
+
+
 def _dense_decode(cfg, x):
     d = L.dims_for(cfg)
     ws = torch.empty(L.msa_dense_decode_workspace_size(d), dtype=torch.uint8, device="cuda")
