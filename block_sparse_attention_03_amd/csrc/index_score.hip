@@ -346,35 +346,55 @@ void index_score_gemm_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 6
     // Only blocks that reach past the group's first position need the causal
     // mask (a workgroup-uniform choice made once per block).
     auto block_body = [&](const unsigned char* kt, int tok_base, float (&mx)[kGTiles], auto masked) {
+        // The 16 (token tile tt, row tile r) products of the block form one
+        // rolling sequence: the four k-steps of each product are interleaved
+        // with the reduction of the previous product (four of its values per
+        // k-step), so the VALU maxima run while the matrix core works.
+        // Value v of a 32x32 result is token tok_base + 32tt + 8(v/4) + 4h +
+        // v%4 of row n.
+        f32x16 prev = {};
+        int prev_lim = 0;
+        auto reduce4 = [&](float m, const f32x16& acc, int q, int lim) {
+#pragma unroll
+            for (int v = 4 * q; v < 4 * q + 4; ++v) {
+                if constexpr (decltype(masked)::value)
+                    m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[v] : -__builtin_inff());
+                else
+                    m = fmaxf(m, acc[v]);
+            }
+            return m;
+        };
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             bf16x8 a[4];
             const unsigned char* arow = kt + (32 * tt + n) * kKStrideB + 64 * h;
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 16 * i));
-            f32x16 acc[kGTiles];
-#pragma unroll
-            for (int r = 0; r < kGTiles; ++r) acc[r] = f32x16{};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < kGTiles; ++r) acc[r] = mfma32(a[i], qb[r][i], acc[r]);
 #pragma unroll
             for (int r = 0; r < kGTiles; ++r) {
+                const int j = tt * kGTiles + r;  // position in the sequence
+                f32x16 acc = {};
                 float m = -__builtin_inff();
-                if constexpr (decltype(masked)::value) {
-                    // value v is token tok_base + 32tt + 8(v/4) + 4h + v%4 of row n
-                    const int lim = prow[r] - tok_base - 32 * tt - 4 * h;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        m = fmaxf(m, (8 * (v / 4) + (v % 4) <= lim) ? acc[r][v] : -__builtin_inff());
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) m = fmaxf(m, acc[r][v]);
+                for (int i = 0; i < 4; ++i) {
+                    acc = mfma32(a[i], qb[r][i], acc);
+                    if (j > 0) m = reduce4(m, prev, i, prev_lim);
+                    // keep the order: one product, then the VALU work beside it
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, decltype(masked)::value ? 8 : 2, 0);
                 }
-                mx[r] = fmaxf(mx[r], m);
+                if (j > 0) {
+                    const int pr = (j - 1) % kGTiles;
+                    mx[pr] = fmaxf(mx[pr], m);
+                }
+                prev = acc;
+                prev_lim = prow[r] - tok_base - 32 * tt - 4 * h;
             }
         }
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = reduce4(m, prev, q, prev_lim);
+        mx[kGTiles - 1] = fmaxf(mx[kGTiles - 1], m);
     };
     auto do_block = [&](int b, int buf, float (&mx)[kGTiles]) {
 #pragma unroll
