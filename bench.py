@@ -59,6 +59,10 @@ def parse():
                     help="only run the headline's index_score_kernel calls (PMC passes)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run chunked-prefill layer-steps, 8192 tokens on 57,344 (PMC passes)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="write the traffic record from four rocprofv3 --pmc counter CSVs "
+                         "(copy calibration FETCH_SIZE, WRITE_SIZE; --score-only FETCH_SIZE, "
+                         "WRITE_SIZE) and exit; needs no GPU")
     return ap.parse_args()
 
 
@@ -290,6 +294,57 @@ def recorded_traffic():
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
+def record_traffic(copy_f, copy_w, fetch, write):
+    """TRAFFIC_FILE from rocprofv3 --pmc counter CSVs: the mean FETCH_SIZE and
+    WRITE_SIZE (KiB) per launch of the headline's index_score_kernel (the ABI
+    form, <true, false>), each scaled by what the same counter reads for a plain
+    256 MiB device copy, with the kernel source's hash so that a later change of
+    the source voids the record."""
+    import csv
+    import hashlib
+    import os
+    from block_sparse_attention_03_amd import accounting as acc
+    from block_sparse_attention_03_amd import inputs as gen
+
+    def mean(path, counter, match):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+        if not vals:
+            raise SystemExit(f"{path}: no {counter} rows for the kernel")
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = 256 << 20
+    is_copy = lambda k: k == "__amd_rocclr_copyBuffer"  # noqa: E731
+    is_score = lambda k: "index_score_kernel<true, false>" in k  # noqa: E731
+    cf, _ = mean(copy_f, "FETCH_SIZE", is_copy)
+    cw, _ = mean(copy_w, "WRITE_SIZE", is_copy)
+    kf, nf = mean(fetch, "FETCH_SIZE", is_score)
+    kw, nw = mean(write, "WRITE_SIZE", is_score)
+    ff, fw = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
+    cfg = gen.config(2)
+    rec = {
+        "kernel": "index_score_kernel",
+        "workload": f"paged decode, {cfg.num_seqs} sequences x {cfg.seq_lens[0]:,} tokens, "
+                    f"H_kv {cfg.num_kv_heads}, H_idx {cfg.num_idx_heads}",
+        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "launches": {"fetch_pass": nf, "write_pass": nw},
+        "fetch_size_kib_per_launch": round(kf, 1),
+        "write_size_kib_per_launch": round(kw, 1),
+        "copy_calibration": {"bytes_per_launch": copy_bytes, "fetch_size_kib": round(cf, 1),
+                             "write_size_kib": round(cw, 1), "fetch_factor": round(ff, 4),
+                             "write_factor": round(fw, 4)},
+        "fetch_bytes_per_launch": int(round(kf * 1024 * ff)),
+        "write_bytes_per_launch": int(round(kw * 1024 * fw)),
+        "algorithmic_bytes_per_launch": acc.score_bytes(cfg),
+    }
+    with open(os.path.join(root, TRAFFIC_FILE), "w") as f:
+        json.dump(rec, f, indent=2)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def measured_ceilings():
     """Sustained HBM read bandwidth and bf16 matrix-core rate on this GPU, from
     the separate calibration library: the best over a few grid sizes of a
@@ -364,6 +419,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

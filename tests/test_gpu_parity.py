@@ -456,21 +456,14 @@ def test_append_then_decode_step_equals_the_full_cache():
     assert torch.equal(step.lse, ref.lse)
 
 
-@pytest.mark.parametrize("hidx", [1, 3])
-def test_decode_step_append_equals_append_then_step(hidx):
-    """msa_decode_step_append (the append done by the scoring launch) leaves
-    the same caches, selection, output and LSE as msa_append_kv followed by
-    msa_decode_step, bit for bit; the caches also equal the oracle's append.
-    The new slots are poisoned with NaN first, so a slot read before it is
-    written shows.  Lengths put the new token at slots 0, 59 and 127 of a
-    block, in the first and in later blocks, with one index head and with one
-    per KV group."""
+def _check_step_append(cfg, seed):
+    """msa_decode_step_append against msa_append_kv + msa_decode_step on copies
+    of the same caches, whose new slots are poisoned with NaN first: caches,
+    selection, output and LSE equal bit for bit, caches equal to the oracle's
+    append."""
     import oracle
-    cfg = gen.MsaConfig("step_append", [9000, 3000, 700, 128, 1, 129], [1] * 6, 12, 3,
-                        permute_pages=True, seed=67).with_idx_heads(hidx)
-    print(f"[step-append] {cfg.name} Hidx={hidx}", flush=True)
     x = gen.make_inputs(cfg, device="cuda")
-    k_new, v_new, i_new = _new_rows(cfg, x, 71)
+    k_new, v_new, i_new = _new_rows(cfg, x, seed)
     seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
     bt = gen.bits(x.block_table)
     pages = torch.tensor([int(bt[s][p // cfg.block_size]) for s, p in zip(seq_of, pos_of)],
@@ -481,6 +474,7 @@ def test_decode_step_append_equals_append_then_step(hidx):
     before = [gen.bits(t) for t in (x.k_cache, x.v_cache, x.kidx_cache)]
     want = oracle.append_kv(*before, gen.bits(k_new), gen.bits(v_new), gen.bits(i_new),
                             bt, cfg.seq_lens, gen.bits(x.cu_q), cfg.block_size)
+    del before
     d = L.dims_for(cfg)
     B, Hq, H = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads
 
@@ -506,6 +500,27 @@ def test_decode_step_append_equals_append_then_step(hidx):
     assert torch.equal(out_b, out_a)
     assert torch.equal(lse_b, lse_a)
     assert torch.isfinite(lse_b).all()
+
+
+@pytest.mark.parametrize("hidx", [1, 3])
+def test_decode_step_append_equals_append_then_step(hidx):
+    """The append inside the decode step's scoring launch
+    (msa_decode_step_append) equals msa_append_kv + msa_decode_step.  Lengths
+    put the new token at slots 0, 59 and 127 of a block, in the first and in
+    later blocks, with one index head and with one per KV group."""
+    cfg = gen.MsaConfig("step_append", [9000, 3000, 700, 128, 1, 129], [1] * 6, 12, 3,
+                        permute_pages=True, seed=67).with_idx_heads(hidx)
+    print(f"[step-append] {cfg.name}", flush=True)
+    _check_step_append(cfg, 71)
+
+
+def test_decode_step_append_rows_past_8192_blocks():
+    """The same equality when a row has more than 8192 blocks, so that the step
+    selects in the standalone kernels after the appending scoring launch."""
+    cfg = gen.MsaConfig("step_append_8300_blocks", [8300 * 128 - 5, 3000], [1, 1], 2, 1,
+                        permute_pages=True, seed=48)
+    print(f"[step-append-past-8192] maxblk={cfg.max_blocks}", flush=True)
+    _check_step_append(cfg, 72)
 
 
 def _dense_decode(cfg, x):
