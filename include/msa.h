@@ -46,7 +46,9 @@
  *     cu_q[s+1]-1 (its n_s new tokens), which are the LAST n_s of its
  *     seq_lens[s] cache tokens: the i-th has absolute position
  *     p = seq_lens[s] - n_s + i and own block b_loc = p / Bk.  Their K, V and
- *     k_idx are already in the cache.  Decode is n_s = 1 for every sequence.
+ *     k_idx are already in the cache (msa_append_kv puts them there;
+ *     msa_decode_step_append does so itself).  Decode is n_s = 1 for every
+ *     sequence.
  *   - Token j of sequence s lives in page block_table[s][j / Bk], slot j % Bk.
  *   - Query head h belongs to KV group h / (H_q / H_kv).
  *   - Supported sizes: head_dim 128, idx_dim 64, block_size 128, topk 16,
