@@ -8,7 +8,9 @@ which holds none of the method's arithmetic.
 
 The arithmetic lives in ``msa_oracle.c`` (plain C, fp64, OpenMP over rows);
 this module only builds it with gcc and marshals numpy arrays.  Each wrapper
-cites the passage it follows in the C file's comments.  bf16 tensors are
+cites the passage it follows in the C file's comments.  The one exception is
+the cache append, a plain copy into the slots of the positions that the C
+code computes, written here with numpy indexing.  bf16 tensors are
 passed as ``uint16`` arrays of raw bits.
 """
 from __future__ import annotations
