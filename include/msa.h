@@ -264,7 +264,9 @@ msa_status_t msa_append_kv(const msa_dims_t *dims, int32_t total_q, const uint16
  *   k_cache, v_cache, kidx_cache: updated in place (only the new slots)
  *   the other arguments as msa_decode_step (same workspace size)
  * The new slots must be distinct; k_new, v_new and kidx_new must not overlap
- * the caches.
+ * the caches; and a page that receives a new token must not appear in another
+ * sequence's block table in the same call (it is written while the other
+ * sequences' blocks are scored: a shared prefix page must be copied first).
  */
 msa_status_t msa_decode_step_append(const msa_dims_t *dims, const uint16_t *k_new,
                                     const uint16_t *v_new, const uint16_t *kidx_new,
