@@ -523,6 +523,42 @@ def test_decode_step_append_rows_past_8192_blocks():
     _check_step_append(cfg, 72)
 
 
+def test_decode_step_append_at_the_headline_size():
+    """The 8 x 60,000 paged decode: msa_decode_step_append against
+    msa_append_kv + msa_decode_step, compared on the GPU (caches, selection,
+    output and LSE bit for bit; each new slot holds exactly the new rows)."""
+    cfg = gen.config(2)
+    print(f"[step-append-headline] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda")
+    k_new, v_new, i_new = _new_rows(cfg, x, 73)
+    d = L.dims_for(cfg)
+    B, Hq, H = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads
+    L_s = torch.tensor(cfg.seq_lens, device="cuda", dtype=torch.long) - 1
+    pages = x.block_table.long()[torch.arange(B, device="cuda"), L_s // cfg.block_size]
+    slots = L_s % cfg.block_size
+
+    def outputs():
+        ws = torch.empty(L.msa_decode_step_workspace_size(d), dtype=torch.uint8, device="cuda")
+        return (torch.empty_like(x.q), torch.empty((B, Hq), dtype=torch.float32, device="cuda"),
+                torch.empty((B, H, cfg.topk), dtype=torch.int32, device="cuda"), ws)
+
+    caches_a = [t.clone() for t in (x.k_cache, x.v_cache, x.kidx_cache)]
+    out_a, lse_a, sel_a, ws_a = outputs()
+    L.msa_append_kv(d, B, k_new, v_new, i_new, x.block_table, x.seq_lens, x.cu_q, *caches_a)
+    L.msa_decode_step(d, x.q_idx, caches_a[2], x.q, caches_a[0], caches_a[1], x.block_table,
+                      x.seq_lens, out_a, lse_a, sel_a, ws_a)
+    out_b, lse_b, sel_b, ws_b = outputs()
+    L.msa_decode_step_append(d, k_new, v_new, i_new, x.q_idx, x.kidx_cache, x.q, x.k_cache,
+                             x.v_cache, x.block_table, x.seq_lens, out_b, lse_b, sel_b, ws_b)
+    torch.cuda.synchronize()
+    for a, b_, new in zip(caches_a, (x.k_cache, x.v_cache, x.kidx_cache), (k_new, v_new, i_new)):
+        assert torch.equal(a, b_)
+        assert torch.equal(b_[pages, :, slots, :].view(torch.int16), new.view(torch.int16))
+    assert torch.equal(sel_b, sel_a)
+    assert torch.equal(out_b, out_a)
+    assert torch.equal(lse_b, lse_a)
+
+
 def _dense_decode(cfg, x):
     d = L.dims_for(cfg)
     ws = torch.empty(L.msa_dense_decode_workspace_size(d), dtype=torch.uint8, device="cuda")
