@@ -294,15 +294,14 @@ def recorded_traffic():
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
-def record_traffic(copy_f, copy_w, fetch, write):
-    """TRAFFIC_FILE from rocprofv3 --pmc counter CSVs: the mean FETCH_SIZE and
-    WRITE_SIZE (KiB) per launch of the headline's index_score_kernel (the ABI
-    form, <true, false>), each scaled by what the same counter reads for a plain
-    256 MiB device copy, with the kernel source's hash so that a later change of
-    the source voids the record."""
+def traffic_record(copy_f, copy_w, fetch, write, src):
+    """The traffic record from rocprofv3 --pmc counter CSVs: the mean
+    FETCH_SIZE and WRITE_SIZE (KiB) per launch of the headline's
+    index_score_kernel (the ABI form, <true, false>), each scaled by what the
+    same counter reads for a plain 256 MiB device copy, with the SHA-256 of
+    the kernel source `src` so that a later change of the source voids it."""
     import csv
     import hashlib
-    import os
     from block_sparse_attention_03_amd import accounting as acc
     from block_sparse_attention_03_amd import inputs as gen
 
@@ -321,10 +320,8 @@ def record_traffic(copy_f, copy_w, fetch, write):
     kf, nf = mean(fetch, "FETCH_SIZE", is_score)
     kw, nw = mean(write, "WRITE_SIZE", is_score)
     ff, fw = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
-    root = os.path.dirname(os.path.abspath(__file__))
-    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
     cfg = gen.config(2)
-    rec = {
+    return {
         "kernel": "index_score_kernel",
         "workload": f"paged decode, {cfg.num_seqs} sequences x {cfg.seq_lens[0]:,} tokens, "
                     f"H_kv {cfg.num_kv_heads}, H_idx {cfg.num_idx_heads}",
@@ -339,6 +336,14 @@ def record_traffic(copy_f, copy_w, fetch, write):
         "write_bytes_per_launch": int(round(kw * 1024 * fw)),
         "algorithmic_bytes_per_launch": acc.score_bytes(cfg),
     }
+
+
+def record_traffic(copy_f, copy_w, fetch, write):
+    """Write TRAFFIC_FILE from the four counter CSVs (see traffic_record)."""
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
+    rec = traffic_record(copy_f, copy_w, fetch, write, src)
     with open(os.path.join(root, TRAFFIC_FILE), "w") as f:
         json.dump(rec, f, indent=2)
         f.write("\n")

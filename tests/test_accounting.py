@@ -37,3 +37,41 @@ def test_attention_flops_follow_the_budget():
     p = [57344 + i for i in range(8192)]
     want = sum(4 * 128 * 48 * (15 * 128 + (x % 128) + 1) for x in p)
     assert acc.attn_flops(cfg) == want
+
+
+def _counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, counter, value) in enumerate(rows):
+            w.writerow([i + 1, name, counter, value])
+
+
+def test_traffic_record_scales_the_counters_by_the_copy(tmp_path):
+    """bench.py's traffic record from rocprofv3 counter CSVs: the mean of the
+    ABI scoring kernel's launches only (not the fused step's copy), scaled by
+    what the counter reads for the 256 MiB copy (FETCH_SIZE half, WRITE_SIZE
+    exact here), keyed by the source's SHA-256."""
+    import hashlib
+    import bench
+    score = "void msa::(anonymous namespace)::index_score_kernel<true, false>(unsigned short const*)"
+    other = "void msa::(anonymous namespace)::index_score_kernel<false, false>(unsigned short const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    p = {k: str(tmp_path / f"{k}.csv") for k in ("cf", "cw", "f", "w")}
+    _counter_csv(p["cf"], [(copy, "FETCH_SIZE", 131072.0), (copy, "FETCH_SIZE", 131072.0),
+                           ("fill", "FETCH_SIZE", 5.0)])
+    _counter_csv(p["cw"], [(copy, "WRITE_SIZE", 262144.0)])
+    _counter_csv(p["f"], [(score, "FETCH_SIZE", 100.0), (score, "FETCH_SIZE", 102.0),
+                          (other, "FETCH_SIZE", 9999.0)])
+    _counter_csv(p["w"], [(score, "WRITE_SIZE", 10.0), (other, "WRITE_SIZE", 7777.0)])
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"kernel source")
+    rec = bench.traffic_record(p["cf"], p["cw"], p["f"], p["w"], str(src))
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0
+    assert rec["copy_calibration"]["write_factor"] == 1.0
+    assert rec["launches"] == {"fetch_pass": 2, "write_pass": 1}
+    assert rec["fetch_bytes_per_launch"] == 101 * 1024 * 2
+    assert rec["write_bytes_per_launch"] == 10 * 1024
+    assert rec["source_sha256"] == hashlib.sha256(b"kernel source").hexdigest()
+    assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(gen.config(2))
