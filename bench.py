@@ -421,7 +421,7 @@ def roofline_entry(name, nbytes, ms, traffic=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
               f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.record_traffic:
