@@ -64,9 +64,16 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
                         int Hkv, int Hidx, int maxblk, AppendRows ap) {
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    const int b = blockIdx.x * kScoreWaves + wave;
-    const int s = blockIdx.y / Hidx;
-    const int ih = blockIdx.y % Hidx;
+    // grid: x = (sequence, index head), y = block chunk, so the sequences vary
+    // fastest in dispatch order; the pair is skewed by the chunk because
+    // workgroups are dealt to the XCDs round-robin: without it sequence s
+    // would always land on XCD s mod 8, and in a ragged batch the XCD holding
+    // the longest rows would finish last
+    const int SH = gridDim.x;
+    const int xs = (int)((blockIdx.x + blockIdx.y) % (unsigned)SH);
+    const int b = blockIdx.y * kScoreWaves + wave;
+    const int s = xs / Hidx;
+    const int ih = xs % Hidx;
     if (b >= maxblk) return;
 
     // the block-table entry (in bounds for any b < maxblk) is read beside the
@@ -472,7 +479,7 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
                            block_table, seq_lens, cu_q, scores, s.B, s.Hkv, s.Hidx, s.maxblk);
         return hipGetLastError();
     }
-    dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
+    dim3 grid(s.B * s.Hidx, ceil_div(s.maxblk, kScoreWaves));
     hipLaunchKernelGGL((index_score_kernel<true, false>), grid, dim3(kScoreWaves * kWave), 0, st,
                        q_idx, kidx, block_table, seq_lens, cu_q, scores, s.Hkv, s.Hidx, s.maxblk,
                        AppendRows{});
@@ -487,7 +494,7 @@ hipError_t msa_launch_index_score_decode(const MsaShape& s, const uint16_t* q_id
     if (s.B == 0) return hipSuccess;
     // scores past each row's own block stay unwritten: the decode step's
     // selection gives blocks past b_loc no key and never reads their values
-    dim3 grid(ceil_div(s.maxblk, kScoreWaves), s.B * s.Hidx);
+    dim3 grid(s.B * s.Hidx, ceil_div(s.maxblk, kScoreWaves));
     if (app) {
         const AppendRows ap{app->kidx_new, app->k_new, app->v_new,
                             app->kidx_cache, app->k_cache, app->v_cache};
