@@ -894,12 +894,14 @@ void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
             acc[2 * e + 1] = ok[i] ? acc[2 * e + 1] + wi * bf16_hi(oi[i][e]) : acc[2 * e + 1];
         }
     }
-    const float inv = 1.0f / den;
+    // a row with no selection attends nothing: out = 0, lse = -inf
+    const bool empty = !(den > 0.f);
+    const float inv = empty ? 0.f : 1.0f / den;
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
     *reinterpret_cast<u32x4*>(out + (size_t)th * kHeadDim + 8 * part) = o;
-    if (lse_out && part == 0) lse_out[th] = mx + __logf(den);
+    if (lse_out && part == 0) lse_out[th] = empty ? -__builtin_inff() : mx + __logf(den);
 }
 
 }  // namespace

@@ -165,7 +165,9 @@ msa_status_t msa_sparse_attn_decode(const msa_dims_t *dims, const uint16_t *q,
  * the selected blocks' tokens, cut at the query position.
  *   q     [total_q, H_q, 128] bf16; sel [total_q, H_kv, k] int32 (ascending or
  *         not; -1 entries ignored; entries must be <= b_loc and unique)
- *   out   [total_q, H_q, 128] bf16 (output); lse [total_q, H_q] fp32 or NULL
+ *   out   [total_q, H_q, 128] bf16 (output); lse [total_q, H_q] fp32 or NULL.
+ *         A (query, group) row whose entries are all -1 attends no token:
+ *         its heads get out = 0 and lse = -inf.
  *   workspace: at least msa_prefill_workspace_size(dims, total_q) bytes,
  *   256-byte aligned; no initial contents required.
  */

@@ -70,10 +70,12 @@ def compact_pages(x, sel_np, seq_of):
     return kp, vp, bt2
 
 
-def check_scores(cfg, x, step, max_rows=4096, seed=0):
+def check_scores(cfg, x, step, max_rows=4096, seed=0, rows=None):
+    """rows: explicit (query * H_kv + group) score rows to compare, else a
+    seeded sample of at most max_rows."""
     seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
     n = cfg.total_q * cfg.num_kv_heads
-    rows = _rows_sample(n, max_rows, seed)
+    rows = _rows_sample(n, max_rows, seed) if rows is None else np.unique(np.asarray(rows, np.int64))
     ref = oracle.index_score(gen.bits(x.q_idx), gen.bits(x.kidx_cache), gen.bits(x.block_table),
                              seq_of, pos_of, cfg.block_size, rows=rows)
     got = step.scores.reshape(n, -1)[torch.from_numpy(rows).to(step.scores.device)].double().cpu().numpy()
@@ -106,11 +108,13 @@ def check_page_table(cfg, x, step):
     assert np.array_equal(step.row_lens.cpu().numpy(), rl), "row lengths differ"
 
 
-def check_attention(cfg, x, step, max_rows=2048, seed=1):
+def check_attention(cfg, x, step, max_rows=2048, seed=1, rows=None):
+    """rows: explicit (query * H_q + head) output rows to compare, else a
+    seeded sample of at most max_rows."""
     seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
     sel = step.sel.cpu().numpy()
     n = cfg.total_q * cfg.num_q_heads
-    rows = _rows_sample(n, max_rows, seed)
+    rows = _rows_sample(n, max_rows, seed) if rows is None else np.unique(np.asarray(rows, np.int64))
     kp, vp, bt2 = compact_pages(x, sel, seq_of)
     ref_o, ref_l = oracle.attention(gen.bits(x.q), kp, vp, bt2, seq_of, pos_of, sel, rows=rows)
     got_o = step.out.reshape(n, -1).float().cpu().numpy()[rows]

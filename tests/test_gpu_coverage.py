@@ -1,0 +1,97 @@
+"""Row widths and edge cases that pick distinct kernel instantiations (needs an
+MI355X; every call goes through the C ABI).
+
+The selection kernels are compiled per row width (max_blocks_per_seq):
+
+  width        msa_topk_blocks            msa_decode_step (fused selection)
+  <= 256       topk_kernel<8, 1>          decode_fused_kernel<4, 1, true>
+  257..512     topk_kernel<8, 1>          decode_fused_kernel<8, 1, true>
+  513..1024    topk_kernel<16, 1>         decode_fused_kernel<16, 1, true>
+  1025..2048   topk_kernel<8, 4>          decode_fused_kernel<8, 4, true>
+  2049..4096   topk_kernel<8, 8>          decode_fused_kernel<16, 4, true>
+  4097..8192   topk_kernel<8, 16>         decode_fused_kernel<32, 4, false>
+  8193..16384  topk_kernel<16, 16>        standalone selection + page kernels
+
+The width is the batch's widest row, so a short row in a wide batch runs the
+wide form with most of its candidate slots empty.  The cases here put a long
+and a short row in each band; each goes through the four calls (checked
+against the oracle, padding poisoned with NaN) and through msa_decode_step
+(bit-equal to the four calls).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_03_amd import inputs as gen
+from block_sparse_attention_03_amd.pipeline import MsaStep
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+BANDS = [
+    # 513..1024 blocks: 16 candidates per lane, one selecting wavefront
+    gen.MsaConfig("band_600_blocks", [76_800, 3_000], [1, 1], 8, 2, permute_pages=True, seed=81),
+    gen.MsaConfig("band_782_blocks", [100_000, 70_000, 3_000], [1, 1, 1], 12, 3,
+                  permute_pages=True, seed=82),
+    gen.MsaConfig("band_1024_blocks", [131_072, 700], [1, 1], 8, 2, permute_pages=True, seed=83),
+    # 4097..8192 blocks: the 16-wavefront selection and the four-wavefront
+    # fused selection without block-table loads, rows partly filled
+    gen.MsaConfig("band_5469_blocks", [700_000, 530_000, 9_000], [1, 1, 1], 4, 2,
+                  permute_pages=True, seed=84),
+    gen.MsaConfig("band_6000_blocks", [6000 * 128 - 77, 5_000], [1, 1], 6, 1,
+                  permute_pages=True, seed=85),
+    gen.MsaConfig("band_8192_blocks_1m_and_5k", [1_048_576, 5_000], [1, 1], 2, 1,
+                  permute_pages=True, seed=86),
+]
+
+
+@pytest.mark.parametrize("cfg", BANDS, ids=lambda c: c.name)
+def test_selection_width_bands(cfg):
+    print(f"[band] {cfg.name} maxblk={cfg.max_blocks} lens={cfg.seq_lens}", flush=True)
+    x, step = parity.full_check(cfg, poison=True)
+    fused = MsaStep(x, fused=True)
+    fused.sel.fill_(-7)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.sel, step.sel)
+    assert torch.equal(fused.out, step.out)
+    assert torch.equal(fused.lse, step.lse)
+
+
+def test_prefill_row_with_no_selection():
+    """A (query, group) row of sel that is all -1 attends no token: its heads
+    get out = 0 and lse = -inf, as the oracle defines the empty token set;
+    the other rows are unchanged and match the oracle."""
+    import oracle
+    cfg = gen.MsaConfig("prefill_empty_rows", [2600, 900], [130, 40], 12, 3, permute_pages=True,
+                        seed=87)
+    print(f"[empty-row] {cfg.name}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    step = MsaStep(x)
+    step.score()
+    step.topk()
+    torch.cuda.synchronize()
+    T, H, G = cfg.total_q, cfg.num_kv_heads, cfg.num_q_heads // cfg.num_kv_heads
+    empty = [(0, 0), (5, 2), (129, 1), (T - 1, 0), (T - 1, 2)]
+    for t, g in empty:
+        step.sel[t, g, :] = -1
+    step.attend()
+    torch.cuda.synchronize()
+    seq_of, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    sel = step.sel.cpu().numpy()
+    kp, vp, bt2 = parity.compact_pages(x, sel, seq_of)
+    ref_o, ref_l = oracle.attention(gen.bits(x.q), kp, vp, bt2, seq_of, pos_of, sel)
+    got_o = step.out.reshape(T * cfg.num_q_heads, -1).float().cpu().numpy()
+    got_l = step.lse.reshape(-1).cpu().numpy()
+    is_empty = np.zeros(T * cfg.num_q_heads, bool)
+    for t, g in empty:
+        is_empty[t * cfg.num_q_heads + g * G: t * cfg.num_q_heads + (g + 1) * G] = True
+    assert np.all(np.isneginf(ref_l[is_empty])) and np.all(ref_o[is_empty] == 0)
+    assert np.all(got_o[is_empty] == 0), "empty rows: out must be 0"
+    assert np.all(np.isneginf(got_l[is_empty])), "empty rows: lse must be -inf"
+    ok = ~is_empty
+    err = np.abs(got_o[ok] - ref_o[ok])
+    assert (err <= parity.OUT_ATOL + parity.OUT_RTOL * np.abs(ref_o[ok])).all()
+    assert np.abs(got_l[ok] - ref_l[ok]).max() <= parity.LSE_ATOL
+

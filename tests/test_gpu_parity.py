@@ -174,8 +174,66 @@ def test_decode_1m_context():
     parity.full_check(gen.config(4))
 
 
+def _prefill_sweep_rows(cfg, x, step, seed=11):
+    """Attention rows (t * H_q + h) of the 8k chunk chosen to cover the
+    block-major kernel's structure, not only a random sample: every head of
+    every query at a block's first and last position (p mod 128 = 0 or 127),
+    every row of the three largest (group, block) buckets (so every 32-row
+    tile of them), one row selecting each nonempty (group, block) bucket, and
+    random rows up to 16,384 or more."""
+    import oracle
+    T, Hq, H = cfg.total_q, cfg.num_q_heads, cfg.num_kv_heads
+    G = Hq // H
+    _, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    sel = step.sel.cpu().numpy()  # [T, H, k]
+    heads = np.arange(Hq)
+    edge_t = np.nonzero((pos_of % cfg.block_size == 0) | (pos_of % cfg.block_size == cfg.block_size - 1))[0]
+    rows = [(edge_t[:, None] * Hq + heads[None, :]).ravel()]
+    # buckets: (group, block) -> the queries that selected it
+    t_idx = np.repeat(np.arange(T), H * cfg.topk)
+    g_idx = np.tile(np.repeat(np.arange(H), cfg.topk), T)
+    b_idx = sel.reshape(-1)
+    keep = b_idx >= 0
+    t_idx, g_idx, b_idx = t_idx[keep], g_idx[keep], b_idx[keep]
+    key = g_idx.astype(np.int64) * cfg.max_blocks + b_idx
+    uniq, first, counts = np.unique(key, return_index=True, return_counts=True)
+    for kb in uniq[np.argsort(-counts, kind="stable")[:3]]:
+        g = int(kb // cfg.max_blocks)
+        ts = t_idx[key == kb]
+        rows.append((ts[:, None] * Hq + g * G + np.arange(G)[None, :]).ravel())
+    # one row per bucket: its first selecting query, a head of its group
+    g_first = (uniq // cfg.max_blocks).astype(np.int64)
+    rows.append(t_idx[first] * Hq + g_first * G + (uniq % G))
+    got = np.unique(np.concatenate(rows))
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(T * Hq, size=max(0, 16384 - got.size) + 2048, replace=False)
+    return np.unique(np.concatenate([got, extra])), len(uniq)
+
+
 def test_chunked_prefill_64k():
-    parity.full_check(gen.config(3), score_rows=512, attn_rows=1024)
+    """The 8192-token chunk on a 57,344-token prefix: every selection row
+    against the oracle's top-k on the GPU's scores; 4,096+ score rows (every
+    group of the queries at block edges, the rest random); 16,384+ attention
+    rows chosen by _prefill_sweep_rows."""
+    import oracle
+    cfg = gen.config(3)
+    x, step = parity.run_step(cfg)
+    T, H = cfg.total_q, cfg.num_kv_heads
+    _, pos_of = oracle.positions(cfg.seq_lens, gen.bits(x.cu_q))
+    edge_t = np.nonzero((pos_of % cfg.block_size == 0) | (pos_of % cfg.block_size == cfg.block_size - 1))[0]
+    edge_rows = (edge_t[:, None] * H + np.arange(H)[None, :]).ravel()
+    others = np.setdiff1d(np.arange(T * H), edge_rows)
+    score_rows = np.unique(np.concatenate([
+        edge_rows, np.random.default_rng(12).choice(others, size=3072, replace=False)]))
+    assert score_rows.size >= 4096
+    s_err = parity.check_scores(cfg, x, step, rows=score_rows)
+    parity.check_selection(cfg, x, step)
+    rows, n_buckets = _prefill_sweep_rows(cfg, x, step)
+    assert rows.size >= 16384 and n_buckets == H * cfg.max_blocks
+    o_err, l_err = parity.check_attention(cfg, x, step, rows=rows)
+    print(f"[parity] {cfg.name}: {score_rows.size} score rows (err/bound {s_err:.3g}), "
+          f"{rows.size} attention rows over {n_buckets} buckets (out max abs {o_err:.3g}, "
+          f"lse max abs {l_err:.3g})", flush=True)
 
 
 def test_paged_decode_60k_per_group_index_keys():
@@ -272,8 +330,10 @@ def test_fused_decode_step_repeats_and_long_rows():
             assert torch.equal(fused.sel, ref.sel), f"{cfg.name} call {i}"
 
 
-@pytest.mark.parametrize("ctx,n_heads", [(60000, (8, 2)), (190000, (4, 1))],
-                         ids=["one_wave_rows", "four_wave_rows"])
+@pytest.mark.parametrize("ctx,n_heads", [(60000, (8, 2)), (100000, (8, 2)), (190000, (4, 1)),
+                                          (700000, (4, 1))],
+                         ids=["one_wave_rows", "one_wave_16_per_lane", "four_wave_rows",
+                              "sixteen_wave_rows"])
 def test_quantised_scores_tie_at_the_threshold(ctx, n_heads):
     """Scores on 100 levels: a few blocks share each level, so the k-th
     largest score is usually tied while only a few dozen blocks reach the
