@@ -29,8 +29,10 @@ EXPORTED = (
     "msa_sparse_attn_prefill", "msa_decode_workspace_size", "msa_prefill_workspace_size",
     "msa_status_string", "msa_abi_version", "msa_decode_step", "msa_decode_step_workspace_size",
     "msa_dense_attn_decode", "msa_dense_decode_workspace_size", "msa_dense_attn_prefill",
-    "msa_validate_inputs", "msa_append_kv", "msa_decode_step_append",
+    "msa_validate_inputs", "msa_append_kv", "msa_decode_step_append", "msa_decode_step_noalloc",
 )
+
+MSA_STATIC_SCRATCH_BYTES = 32 << 20  # include/msa.h
 
 
 class msa_dims_t(ctypes.Structure):
@@ -75,6 +77,7 @@ def lib():
         L.msa_sparse_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.msa_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.msa_decode_step_append.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.msa_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
         L.msa_decode_step_workspace_size.argtypes = [D]
         L.msa_decode_step_workspace_size.restype = SZ
         L.msa_dense_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
@@ -86,7 +89,7 @@ def lib():
         for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
                   "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_decode_step",
                   "msa_dense_attn_decode", "msa_dense_attn_prefill", "msa_validate_inputs",
-                  "msa_append_kv", "msa_decode_step_append"):
+                  "msa_append_kv", "msa_decode_step_append", "msa_decode_step_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_decode_workspace_size.argtypes = [D]
         L.msa_decode_workspace_size.restype = SZ
@@ -314,6 +317,37 @@ def msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, s
                     sel, workspace, stream=None):
     prepare_msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens,
                             out, lse, sel, workspace)(stream)
+
+
+def prepare_msa_decode_step_noalloc(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table,
+                                    seq_lens, out, lse, sel):
+    """msa_decode_step_noalloc (the decode step in the library's own static
+    scratch, no workspace) with its arguments checked and packed once: returns
+    a PreparedCall that repeats the call, on the current (or a given) stream."""
+    d = dims
+    B, Hq, H = d.num_seqs, d.num_q_heads, d.num_kv_heads
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    args = (_ptr(q_idx, BF16, "q_idx", (B, H, d.idx_dim)),
+            _ptr(kidx_cache, BF16, "kidx_cache", (d.num_pages, d.num_idx_heads, d.block_size, d.idx_dim)),
+            _ptr(q, BF16, "q", (B, Hq, d.head_dim)), _ptr(k_cache, BF16, "k_cache", cache),
+            _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)),
+            _ptr(out, BF16, "out", (B, Hq, d.head_dim)),
+            _ptr(lse, F32, "lse", (B, Hq)) if lse is not None else None,
+            _ptr(sel, I32, "sel", (B, H, d.topk)) if sel is not None else None)
+    return PreparedCall(lib().msa_decode_step_noalloc, (ctypes.byref(d), *args),
+                        "msa_decode_step_noalloc",
+                        (d, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
+                         lse, sel))
+
+
+def msa_decode_step_noalloc(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens,
+                            out, lse, sel, stream=None):
+    """msa_decode_step without a workspace: the library's static per-GPU scratch
+    (MSA_STATIC_SCRATCH_BYTES) holds the step's partials; nothing is allocated."""
+    prepare_msa_decode_step_noalloc(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table,
+                                    seq_lens, out, lse, sel)(stream)
 
 
 def prepare_msa_decode_step_append(dims, k_new, v_new, kidx_new, q_idx, kidx_cache, q, k_cache,

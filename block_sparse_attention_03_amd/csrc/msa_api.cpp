@@ -54,6 +54,11 @@ msa_status_t check_total_q(const MsaShape& s, int32_t total_q) {
 
 msa_status_t launched(hipError_t e) { return e == hipSuccess ? MSA_SUCCESS : MSA_ERROR_LAUNCH; }
 
+// Marks a decode step that runs in the library's static scratch: a tag
+// compared by address, never dereferenced or passed to a kernel.
+char g_static_scratch_tag;
+void* const kStaticScratch = &g_static_scratch_tag;
+
 }  // namespace
 
 extern "C" {
@@ -169,7 +174,8 @@ size_t msa_decode_step_workspace_size(const msa_dims_t* dims) {
     return msa_decode_step_ws_bytes(s);
 }
 
-// The decode step's checks and launches, with or without the cache append.
+// The decode step's checks and launches, with or without the cache append;
+// workspace == kStaticScratch selects the library's static scratch.
 static msa_status_t decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
                                 const uint16_t* kidx_cache, const uint16_t* q,
                                 const uint16_t* k_cache, const uint16_t* v_cache,
@@ -191,11 +197,17 @@ static msa_status_t decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
         (sel && !aligned(sel, 4)))
         return MSA_ERROR_INVALID_VALUE;
     if ((int64_t)s.B * s.Hidx > 65535) return MSA_ERROR_NOT_SUPPORTED;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < msa_decode_step_ws_bytes(s))
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (workspace == kStaticScratch) {
+        // the library's own scratch on the stream's GPU, no caller workspace
+        if (msa_decode_step_ws_bytes(s) > msa_static_scratch_bytes()) return MSA_ERROR_WORKSPACE;
+        if (msa_static_scratch(hs, &workspace) != hipSuccess) return MSA_ERROR_LAUNCH;
+    } else if (!workspace || !aligned(workspace, 256) ||
+               workspace_bytes < msa_decode_step_ws_bytes(s)) {
         return MSA_ERROR_WORKSPACE;
+    }
     return launched(msa_launch_decode_step(s, q_idx, kidx_cache, q, k_cache, v_cache, block_table,
-                                           seq_lens, out, lse, sel, workspace, app,
-                                           static_cast<hipStream_t>(stream)));
+                                           seq_lens, out, lse, sel, workspace, app, hs));
 }
 
 msa_status_t msa_decode_step(const msa_dims_t* dims, const uint16_t* q_idx,
@@ -218,6 +230,15 @@ msa_status_t msa_decode_step_append(const msa_dims_t* dims, const uint16_t* k_ne
     const DecodeAppend app{k_new, v_new, kidx_new, k_cache, v_cache, kidx_cache};
     return decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
                        lse, sel, workspace, workspace_bytes, &app, stream);
+}
+
+msa_status_t msa_decode_step_noalloc(const msa_dims_t* dims, const uint16_t* q_idx,
+                                     const uint16_t* kidx_cache, const uint16_t* q,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     uint16_t* out, float* lse, int32_t* sel, void* stream) {
+    return decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, out,
+                       lse, sel, kStaticScratch, 0, nullptr, stream);
 }
 
 size_t msa_dense_decode_workspace_size(const msa_dims_t* dims) {

@@ -186,3 +186,7 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
                                   const int32_t* seq_lens, uint16_t* out, float* lse,
                                   int32_t* sel_out, void* ws, const DecodeAppend* app,
                                   hipStream_t st);
+// The library's static device scratch (static_scratch.hip): its size, and its
+// device address on the device of `st`, looked up once per device.
+size_t msa_static_scratch_bytes();
+hipError_t msa_static_scratch(hipStream_t st, void** out);

@@ -204,6 +204,29 @@ msa_status_t msa_decode_step(const msa_dims_t *dims, const uint16_t *q_idx,
                              void *stream);
 
 /*
+ * msa_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation): the
+ * same launches and results, bit for bit, with no workspace argument.  The
+ * step's scratch (page partials, block scores, row lengths) is a fixed array
+ * of MSA_STATIC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing.  Arguments as msa_decode_step; the work runs on the GPU of
+ * `stream`.
+ *   Returns MSA_ERROR_WORKSPACE, launching nothing, when
+ *   msa_decode_step_workspace_size(dims) exceeds MSA_STATIC_SCRATCH_BYTES.
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents (no call depends on them): calls ordered on one stream are fine,
+ * while calls that may overlap on one GPU (unordered streams) race and give
+ * wrong results.
+ */
+#define MSA_STATIC_SCRATCH_BYTES (32u << 20)
+msa_status_t msa_decode_step_noalloc(const msa_dims_t *dims, const uint16_t *q_idx,
+                                     const uint16_t *kidx_cache, const uint16_t *q,
+                                     const uint16_t *k_cache, const uint16_t *v_cache,
+                                     const int32_t *block_table, const int32_t *seq_lens,
+                                     uint16_t *out, float *lse, int32_t *sel, void *stream);
+
+/*
  * Dense GQA decode attention, the baseline MSA's decode speedup is measured
  * against ([youmind] bullet "Rapido en produccion": decode vs dense GQA with
  * the same heads): every query head of sequence s attends all seq_lens[s]

@@ -207,3 +207,25 @@ def test_validate_inputs_errors():
     assert lib.msa_validate_inputs(ctypes.byref(d), -1, A, A, A, A, None) == L.MSA_ERROR_INVALID_VALUE
     bad = dims(topk=8)
     assert lib.msa_validate_inputs(ctypes.byref(bad), 5, A, A, A, A, None) == L.MSA_ERROR_NOT_SUPPORTED
+
+
+def test_decode_step_noalloc_host_checks():
+    """msa_decode_step_noalloc: no work succeeds without pointers; NULL or
+    misaligned pointers are refused; a shape whose decode-step scratch exceeds
+    MSA_STATIC_SCRATCH_BYTES is refused with MSA_ERROR_WORKSPACE before any
+    HIP call (so these run without a GPU)."""
+    lib = L.lib()
+    N = None
+    assert lib.msa_decode_step_noalloc(ctypes.byref(dims(num_seqs=0)), N, N, N, N, N, N, N, N, N,
+                                       N, N) == L.MSA_SUCCESS
+    d = dims()
+    assert lib.msa_decode_step_noalloc(ctypes.byref(d), N, A, A, A, A, A, A, A, N, N,
+                                       N) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_decode_step_noalloc(ctypes.byref(d), A, A, A, A, A, A, A, MIS, N, N,
+                                       N) == L.MSA_ERROR_INVALID_VALUE
+    big = dims(num_seqs=512, num_q_heads=16, num_kv_heads=2)
+    assert L.msa_decode_step_workspace_size(big) > L.MSA_STATIC_SCRATCH_BYTES
+    assert lib.msa_decode_step_noalloc(ctypes.byref(big), A, A, A, A, A, A, A, A, A, A,
+                                       N) == L.MSA_ERROR_WORKSPACE
+    assert lib.msa_decode_step_noalloc(ctypes.byref(dims(head_dim=64)), A, A, A, A, A, A, A, A, A,
+                                       A, N) == L.MSA_ERROR_NOT_SUPPORTED
