@@ -57,12 +57,16 @@ def parse():
                     help="only run plain 256 MiB device copies (PMC byte-counter calibration)")
     ap.add_argument("--score-only", action="store_true",
                     help="only run the headline's index_score_kernel calls (PMC passes)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only run the headline's msa_decode_step layer-steps (PMC passes)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run chunked-prefill layer-steps, 8192 tokens on 57,344 (PMC passes)")
-    ap.add_argument("--record-traffic", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
-                    help="write the traffic record from four rocprofv3 --pmc counter CSVs "
-                         "(copy calibration FETCH_SIZE, WRITE_SIZE; --score-only FETCH_SIZE, "
-                         "WRITE_SIZE) and exit; needs no GPU")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("RECORD", "COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="write traffic record RECORD (index_score: --score-only passes; "
+                         "decode_step: --step-only passes) from four rocprofv3 --pmc counter "
+                         "CSVs (copy calibration FETCH_SIZE, WRITE_SIZE; the workload's "
+                         "FETCH_SIZE, WRITE_SIZE) and exit; needs no GPU")
     return ap.parse_args()
 
 
@@ -240,23 +244,109 @@ def make_layers(cfg, n, device="cuda"):
             for l in range(n)]
 
 
-def cpu_baseline(cfg, x, budget_s):
-    """The oracle (as it stands) on the same decode workload, full layer-steps."""
-    import oracle
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _host(x, names):
     from block_sparse_attention_03_amd import inputs as gen
-    host = {k: gen.bits(getattr(x, k)) for k in
-            ("q_idx", "kidx_cache", "q", "k_cache", "v_cache", "block_table", "seq_lens", "cu_q")}
+    return {k: gen.bits(getattr(x, k)) for k in names}
+
+
+def _selected_pages(x, sel, seq_of):
+    """Host copies of the K/V pages a selection touches, and a block table
+    mapping each selected (sequence, block) to its row in them (others -> 0):
+    the oracle's attention then reads only those pages from host memory."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_03_amd import inputs as gen
+    bt = gen.bits(x.block_table)
+    T = sel.shape[0]
+    pairs = np.unique(np.stack([np.repeat(seq_of[:T], sel.shape[1] * sel.shape[2]),
+                                sel.reshape(-1)], axis=1), axis=0)
+    pairs = pairs[pairs[:, 1] >= 0]
+    pages = torch.from_numpy(bt[pairs[:, 0], pairs[:, 1]].astype(np.int64)).to(x.k_cache.device)
+    kp = gen.bits(x.k_cache.index_select(0, pages))
+    vp = gen.bits(x.v_cache.index_select(0, pages))
+    bt2 = np.zeros_like(bt)
+    bt2[pairs[:, 0], pairs[:, 1]] = np.arange(len(pairs), dtype=np.int32)
+    return kp, vp, bt2
+
+
+def cpu_stages(cfg, x, sample_queries=None):
+    """Wall seconds of the oracle's stages on one layer-step of `cfg` (inputs
+    `x`, already drawn on the GPU): scoring, top-k, page table (decode) and
+    attention.  sample_queries: score, select and attend only that many query
+    tokens of each sequence, evenly spaced over its new tokens, and scale the
+    stage times to the whole step by the query count.  Host copies are not
+    timed."""
+    import numpy as np
+    import oracle
+    h = _host(x, ("q_idx", "kidx_cache", "q", "block_table", "seq_lens", "cu_q"))
+    H, Hq, k = cfg.num_kv_heads, cfg.num_q_heads, cfg.topk
+    seq_of, pos_of = oracle.positions(h["seq_lens"], h["cu_q"])
+    T = cfg.total_q
+    # a sample: sample_queries query tokens of each sequence, evenly spaced
+    # over its query range (so their positions span the chunk's)
+    toks = np.arange(T) if sample_queries is None else np.unique(np.concatenate(
+        [a + (np.arange(min(sample_queries, b - a)) * (b - a)) // max(1, min(sample_queries, b - a))
+         for a, b in zip(h["cu_q"][:-1].astype(np.int64), h["cu_q"][1:].astype(np.int64))]))
+    n = len(toks)
+    score_rows = (toks[:, None] * H + np.arange(H)[None, :]).ravel()
+    t0 = time.perf_counter()
+    sc = oracle.index_score(h["q_idx"], h["kidx_cache"], h["block_table"], seq_of, pos_of,
+                            cfg.block_size, rows=score_rows)
+    t1 = time.perf_counter()
+    bl = oracle.b_loc_rows(pos_of, H, cfg.block_size)[score_rows]
+    chosen = oracle.topk(sc, bl, k)
+    t2 = time.perf_counter()
+    sel = np.full((T, H, k), -1, np.int32)
+    sel[toks] = chosen.reshape(n, H, k)
+    pt_s = 0.0
+    if cfg.is_decode and sample_queries is None:
+        t3 = time.perf_counter()
+        oracle.page_table(sel, h["block_table"], h["seq_lens"], cfg.block_size)
+        pt_s = time.perf_counter() - t3
+    kp, vp, bt2 = _selected_pages(x, sel, seq_of)
+    attn_rows = (toks[:, None] * Hq + np.arange(Hq)[None, :]).ravel()
+    t4 = time.perf_counter()
+    oracle.attention(h["q"], kp, vp, bt2, seq_of, pos_of, sel, rows=attn_rows)
+    t5 = time.perf_counter()
+    f = T / n
+    st = {"score": (t1 - t0) * f, "topk": (t2 - t1) * f, "page_table": pt_s * f,
+          "attention": (t5 - t4) * f}
+    out = {"step_s": round(sum(st.values()), 4),
+           "stage_s": {a: round(b, 5) for a, b in st.items()},
+           "sample": "the whole layer-step" if n == T else
+                     f"{n} of {T} query tokens ({sample_queries} per sequence, evenly spaced "
+                     f"over its new tokens), stage times scaled by {T}/{n}"}
+    return out
+
+
+def cpu_baseline(cfg, x, budget_s):
+    """The oracle (as it stands) on the same decode workload, full layer-steps,
+    repeated for about budget_s seconds."""
+    import oracle
+    h = _host(x, ("q_idx", "kidx_cache", "q", "k_cache", "v_cache", "block_table", "seq_lens",
+                  "cu_q"))
     oracle.build(force=False)
     H = cfg.num_kv_heads
 
     def one_step():
-        seq_of, pos_of = oracle.positions(host["seq_lens"], host["cu_q"])
-        sc = oracle.index_score(host["q_idx"], host["kidx_cache"], host["block_table"], seq_of,
+        seq_of, pos_of = oracle.positions(h["seq_lens"], h["cu_q"])
+        sc = oracle.index_score(h["q_idx"], h["kidx_cache"], h["block_table"], seq_of,
                                 pos_of, cfg.block_size)
         sel = oracle.topk(sc, oracle.b_loc_rows(pos_of, H, cfg.block_size), cfg.topk)
         sel = sel.reshape(cfg.total_q, H, cfg.topk)
-        oracle.page_table(sel, host["block_table"], host["seq_lens"], cfg.block_size)
-        oracle.attention(host["q"], host["k_cache"], host["v_cache"], host["block_table"],
+        oracle.page_table(sel, h["block_table"], h["seq_lens"], cfg.block_size)
+        oracle.attention(h["q"], h["k_cache"], h["v_cache"], h["block_table"],
                          seq_of, pos_of, sel)
 
     n, t0 = 0, time.perf_counter()
@@ -267,43 +357,75 @@ def cpu_baseline(cfg, x, budget_s):
         if el >= budget_s or n >= 5000:
             break
     return {"value": round(el * 1e6 / n, 1), "unit": "us/layer-step", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n} full layer-steps of the headline workload (64 rows scored over "
                       f"60,000 tokens each, top-k, page table, attention), fp64 C with OpenMP, "
-                      f"{el:.1f} s"}
+                      f"{el:.1f} s",
+            "stages": cpu_stages(cfg, x)}
 
 
-TRAFFIC_FILE = "profiles/index_score_decode_60k_traffic.json"
+# Traffic records: HBM bytes per launch (per layer-step for the decode step)
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, keyed by the SHA-256 of the
+# sources the kernels are built from, so that a later change voids them.
+CSRC = "block_sparse_attention_03_amd/csrc"
+TRAFFIC = {
+    "index_score": {
+        "file": "profiles/index_score_decode_60k_traffic.json",
+        "sources": ["index_score.hip"],
+        "kernels": ["index_score_kernel<true, false>"],
+        "what": "index_score_kernel (the msa_index_score form) per launch",
+    },
+    "decode_step": {
+        "file": "profiles/decode_step_60k_traffic.json",
+        "sources": ["index_score.hip", "decode_attn.hip", "select.hpp", "decode_tile.hpp",
+                    "msa_common.hpp"],
+        "kernels": ["index_score_kernel<false, false>", "decode_fused_kernel<8, 1, true>",
+                    "decode_merge_kernel"],
+        "what": "msa_decode_step's three kernels, summed per layer-step",
+    },
+}
 
 
-def recorded_traffic():
-    """HBM bytes per launch of index_score_kernel on the headline workload, from
-    the FETCH_SIZE and WRITE_SIZE passes recorded in TRAFFIC_FILE -- or None if
-    the kernel's source has changed since they were taken."""
-    import hashlib
+def _root():
     import os
-    root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, TRAFFIC_FILE)
-    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
+    return os.path.dirname(os.path.abspath(__file__))
+
+
+def sources_sha256(srcs):
+    """SHA-256 over the bytes of the source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in srcs:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch (per layer-step for decode_step) from the traffic
+    record `name`, or None if a source has changed since it was taken."""
+    import os
+    spec = TRAFFIC[name]
+    path = os.path.join(_root(), spec["file"])
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    srcs = [os.path.join(_root(), CSRC, f) for f in spec["sources"]]
+    if rec.get("source_sha256") != sources_sha256(srcs):
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
-def traffic_record(copy_f, copy_w, fetch, write, src):
-    """The traffic record from rocprofv3 --pmc counter CSVs: the mean
-    FETCH_SIZE and WRITE_SIZE (KiB) per launch of the headline's
-    index_score_kernel (the ABI form, <true, false>), each scaled by what the
-    same counter reads for a plain 256 MiB device copy, with the SHA-256 of
-    the kernel source `src` so that a later change of the source voids it."""
+def traffic_record(name, copy_f, copy_w, fetch, write, srcs):
+    """Traffic record `name` from rocprofv3 --pmc counter CSVs: for each of the
+    record's kernels, the mean FETCH_SIZE and WRITE_SIZE (KiB) over its
+    launches, each scaled by what the same counter reads for a plain 256 MiB
+    device copy; the record's totals sum its kernels (one launch each per
+    layer-step); `srcs` are hashed into the record."""
     import csv
-    import hashlib
     from block_sparse_attention_03_amd import accounting as acc
     from block_sparse_attention_03_amd import inputs as gen
+    spec = TRAFFIC[name]
 
     def mean(path, counter, match):
         vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
@@ -314,37 +436,45 @@ def traffic_record(copy_f, copy_w, fetch, write, src):
 
     copy_bytes = 256 << 20
     is_copy = lambda k: k == "__amd_rocclr_copyBuffer"  # noqa: E731
-    is_score = lambda k: "index_score_kernel<true, false>" in k  # noqa: E731
     cf, _ = mean(copy_f, "FETCH_SIZE", is_copy)
     cw, _ = mean(copy_w, "WRITE_SIZE", is_copy)
-    kf, nf = mean(fetch, "FETCH_SIZE", is_score)
-    kw, nw = mean(write, "WRITE_SIZE", is_score)
     ff, fw = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    kernels = []
+    for kname in spec["kernels"]:
+        kf, nf = mean(fetch, "FETCH_SIZE", lambda k, kn=kname: kn in k)
+        kw, nw = mean(write, "WRITE_SIZE", lambda k, kn=kname: kn in k)
+        kernels.append({"kernel": kname, "launches": {"fetch_pass": nf, "write_pass": nw},
+                        "fetch_size_kib_per_launch": round(kf, 1),
+                        "write_size_kib_per_launch": round(kw, 1),
+                        "fetch_bytes_per_launch": int(round(kf * 1024 * ff)),
+                        "write_bytes_per_launch": int(round(kw * 1024 * fw))})
     cfg = gen.config(2)
+    algo = acc.score_bytes(cfg) + (acc.decode_attn_bytes(cfg) if name == "decode_step" else 0)
     return {
-        "kernel": "index_score_kernel",
+        "record": name,
+        "what": spec["what"],
         "workload": f"paged decode, {cfg.num_seqs} sequences x {cfg.seq_lens[0]:,} tokens, "
                     f"H_kv {cfg.num_kv_heads}, H_idx {cfg.num_idx_heads}",
-        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
-        "launches": {"fetch_pass": nf, "write_pass": nw},
-        "fetch_size_kib_per_launch": round(kf, 1),
-        "write_size_kib_per_launch": round(kw, 1),
+        "source_sha256": sources_sha256(srcs),
+        "sources": [f"{CSRC}/{f}" for f in spec["sources"]],
+        "kernels": kernels,
         "copy_calibration": {"bytes_per_launch": copy_bytes, "fetch_size_kib": round(cf, 1),
                              "write_size_kib": round(cw, 1), "fetch_factor": round(ff, 4),
                              "write_factor": round(fw, 4)},
-        "fetch_bytes_per_launch": int(round(kf * 1024 * ff)),
-        "write_bytes_per_launch": int(round(kw * 1024 * fw)),
-        "algorithmic_bytes_per_launch": acc.score_bytes(cfg),
+        "fetch_bytes_per_launch": sum(k["fetch_bytes_per_launch"] for k in kernels),
+        "write_bytes_per_launch": sum(k["write_bytes_per_launch"] for k in kernels),
+        "algorithmic_bytes_per_launch": algo,
     }
 
 
-def record_traffic(copy_f, copy_w, fetch, write):
-    """Write TRAFFIC_FILE from the four counter CSVs (see traffic_record)."""
+def record_traffic(name, copy_f, copy_w, fetch, write):
+    """Write traffic record `name` from the four counter CSVs (see traffic_record)."""
     import os
-    root = os.path.dirname(os.path.abspath(__file__))
-    src = os.path.join(root, "block_sparse_attention_03_amd", "csrc", "index_score.hip")
-    rec = traffic_record(copy_f, copy_w, fetch, write, src)
-    with open(os.path.join(root, TRAFFIC_FILE), "w") as f:
+    if name not in TRAFFIC:
+        raise SystemExit(f"unknown traffic record {name!r}: one of {sorted(TRAFFIC)}")
+    srcs = [os.path.join(_root(), CSRC, f) for f in TRAFFIC[name]["sources"]]
+    rec = traffic_record(name, copy_f, copy_w, fetch, write, srcs)
+    with open(os.path.join(_root(), TRAFFIC[name]["file"]), "w") as f:
         json.dump(rec, f, indent=2)
         f.write("\n")
     print(json.dumps(rec))
@@ -457,6 +587,12 @@ def main():
         ms = time_calls([s_.score for s_ in four], args.steps, args.warmup)
         print(json.dumps({"index_score_ms": ms, "launches": args.steps + args.warmup}))
         return
+    if args.step_only:
+        cfg = gen.config(2)
+        fused = [MsaStep(x, fused=True) for x in make_layers(cfg, args.layers)]
+        ms = time_calls([s_.run for s_ in fused], args.steps, args.warmup)
+        print(json.dumps({"decode_step_ms": ms, "layer_steps": args.steps + args.warmup}))
+        return
 
     # ---------------- headline: paged decode at 60k, batch 8 ----------------
     cfg = gen.config(2)
@@ -466,8 +602,7 @@ def main():
     fused_ms = time_calls([s.run for s in fused], args.steps, args.warmup)
     four_ms = time_calls([s.run for s in four], args.steps, args.warmup)
     graph_ms = time_graph(fused, args.steps, args.warmup)
-    # roofline kernel: index_score_kernel, a single-kernel call (it and the
-    # page kernel each move about half of the step's bytes)
+    # the scoring pass alone (msa_index_score: the same index_score_kernel)
     score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
     attn_ms = time_calls([s.attend for s in four], args.steps, args.warmup)
     topk_line = {cfg.name: topk_vs_torch(four, args.steps)}
@@ -497,10 +632,17 @@ def main():
                    "seed": cfg.seed, "layers": args.layers,
                    "timing": "layer-steps back to back over distinct per-layer caches (cold HBM)",
                    "entry_point": "msa_decode_step"},
-        "roofline": roofline_entry("index_score_kernel", acc.score_bytes(cfg), score_ms,
-                                   recorded_traffic()),
+        # the timed step is msa_decode_step's three kernels, one launch each;
+        # the select-and-attend kernel is the longest of them (kernel trace)
+        "roofline": dict(roofline_entry(
+            "msa_decode_step: index_score_kernel + decode_fused_kernel<8,1,true> + "
+            "decode_merge_kernel", layer_bytes, fused_ms, recorded_traffic("decode_step")),
+            launches_per_step=3),
         "layer_step": {"algorithmic_bytes": layer_bytes,
                        "hbm_frac": frac(fused_ms),
+                       "scoring_pass": roofline_entry("index_score_kernel", acc.score_bytes(cfg),
+                                                      score_ms, recorded_traffic("index_score")),
+                       "select_attend_merge_us": round((fused_ms - score_ms) * 1e3, 2),
                        "us_hip_graph": round(graph_ms * 1e3, 2),
                        "us_four_calls": round(four_ms * 1e3, 2),
                        "hbm_frac_four_calls": frac(four_ms),
@@ -521,14 +663,21 @@ def main():
         result["roofline"]["achieved"] / ceil["hbm_read_gbs"], 4)
     result["roofline"]["frac_of_measured_64mib"] = round(
         result["roofline"]["achieved"] / ceil["hbm_read_64mib_gbs"], 4)
+    sp = result["layer_step"]["scoring_pass"]
+    sp["frac_of_measured_64mib"] = round(sp["achieved"] / ceil["hbm_read_64mib_gbs"], 4)
     result["layer_step"]["hbm_frac_of_measured"] = round(
         result["layer_step"]["hbm_frac"] * acc.HBM_PEAK_GBS / ceil["hbm_read_gbs"], 4)
 
     if not args.no_also:
         also = {}
 
-        def decode_line(c, n_layers, n_steps, graph=False):
+        cpu_cfg = {}  # the oracle's stages per workload (CPU baseline)
+        want_cpu = not args.no_cpu_baseline
+
+        def decode_line(c, n_layers, n_steps, graph=False, cpu=False):
             ls = make_layers(c, n_layers)
+            if cpu and want_cpu:
+                cpu_cfg[c.name] = cpu_stages(c, ls[0])
             f = [MsaStep(x, fused=True) for x in ls]
             fo = [MsaStep(x) for x in ls]
             ms_ = time_calls([st.run for st in f], n_steps, 4)
@@ -546,13 +695,13 @@ def main():
 
         # decode at 4096 tokens, batch 1 (2.6 MB: launch-bound)
         c1 = gen.config(1)
-        also[c1.name] = decode_line(c1, 128, max(128, args.steps), graph=True)
+        also[c1.name] = decode_line(c1, 128, max(128, args.steps), graph=True, cpu=True)
         # the 60k decode with one index key per KV group (H_idx = H_kv): 558 MB
         cg = gen.config(2).with_idx_heads(gen.config(2).num_kv_heads)
         also["paged_decode_b8_ctx60k_per_group_index_keys"] = decode_line(cg, 4, max(40, args.steps // 4))
         # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
         c5 = gen.config(5)
-        also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4))
+        also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4), cpu=True)
         # multi-query decode: 4 draft tokens per sequence on the 60k workload,
         # through msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill
         import dataclasses
@@ -569,6 +718,8 @@ def main():
         # 1M-context decode, batch 4 (18 GB of K/V per layer): 2 layers
         c4 = gen.config(4)
         l4 = make_layers(c4, 2)
+        if want_cpu:
+            cpu_cfg[c4.name] = cpu_stages(c4, l4[0])
         f4 = [MsaStep(x, fused=True) for x in l4]
         s4 = [MsaStep(x) for x in l4]
         n4 = max(10, args.steps // 8)
@@ -585,6 +736,8 @@ def main():
         # chunked prefill: 8192 new tokens on a 57,344-token prefix, 2 layers
         c3 = gen.config(3)
         l3 = make_layers(c3, 2)
+        if want_cpu:
+            cpu_cfg[c3.name] = cpu_stages(c3, l3[0], sample_queries=32)
         s3 = [MsaStep(x) for x in l3]
         n3 = max(6, args.steps // 25)
         ms3 = time_calls([s.run for s in s3], n3, 2)
@@ -628,6 +781,9 @@ def main():
         del s3, l3
         torch.cuda.empty_cache()
         result["also"] = also
+        if want_cpu:
+            cb = result["cpu_baseline"]
+            cb["per_config"] = {cfg.name: cb.pop("stages"), **cpu_cfg}
 
     print(json.dumps(result), flush=True)
 

@@ -25,14 +25,14 @@ namespace msa {
 namespace {
 
 struct DecodeWs {
-    float* o;    // [R, k, G, 128] normalised partial outputs
-    float* lse;  // [R, k, G]
+    uint16_t* o;  // [R, k, G, 128] normalised partial outputs, bf16
+    float* lse;   // [R, k, G]
 };
 
 __device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
     DecodeWs w;
-    w.o = static_cast<float*>(ws);
-    w.lse = w.o + (size_t)R * kTopK * G * kHeadDim;
+    w.o = static_cast<uint16_t*>(ws);
+    w.lse = reinterpret_cast<float*>(w.o + (size_t)R * kTopK * G * kHeadDim);
     return w;
 }
 
@@ -157,12 +157,13 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
         if (n < G) {
             DecodeWs w = decode_ws(ws, R, G);
             const float inv = 1.0f / l;
-            float* orow = w.o + (((size_t)r * kTopK + slot) * G + n) * kHeadDim;
+            uint16_t* orow = w.o + (((size_t)r * kTopK + slot) * G + n) * kHeadDim;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int d = 32 * wave + 16 * mt + 4 * kg;
-                f32x4 o = oacc[mt] * inv;
-                *reinterpret_cast<f32x4*>(orow + d) = o;
+                *reinterpret_cast<u32x2*>(orow + d) =
+                    u32x2{pack2_bf16(oacc[mt][0] * inv, oacc[mt][1] * inv),
+                          pack2_bf16(oacc[mt][2] * inv, oacc[mt][3] * inv)};
             }
             if (wave == 0 && kg == 0)
                 w.lse[((size_t)r * kTopK + slot) * G + n] = m * scale_log2 * kLn2 + __logf(l);
@@ -255,42 +256,68 @@ void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
                 scale_log2, sh);
 }
 
-// One thread per (row, head, dim): Log-Sum-Exp merge of the row's pages.
-__global__ __launch_bounds__(kHeadDim)
+// Log-Sum-Exp merge of a row's pages: 16 threads per (row, head), each
+// merging 8 dims (one 16-byte piece of every page's bf16 partial); four
+// (row, head) pairs per 64-thread workgroup.
+constexpr int kMergeThreads = 64;
+
+__global__ __launch_bounds__(kMergeThreads)
 void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __restrict__ ws,
                          uint16_t* __restrict__ out, float* __restrict__ lse_out, int Hq,
                          int Hkv, int R) {
-    const int rn = blockIdx.x;  // r * G + n
+    const int idx = blockIdx.x * kMergeThreads + threadIdx.x;
     const int G = Hq / Hkv;
+    const int rn = idx / 16;  // r * G + n
+    const int part = idx % 16;
+    if (rn >= R * G) return;
     const int r = rn / G;
     const int n = rn % G;
-    const int d = threadIdx.x;
     DecodeWs w = decode_ws(const_cast<void*>(ws), R, G);
     const float* lp = w.lse + (size_t)r * kTopK * G + n;
     // every slot's partial is loaded together with the row length (slots past
     // the row's pages hold stale workspace values and are dropped by selects,
     // never by a multiply, so a stale non-finite value cannot leak in)
-    float li[kTopK], oi[kTopK];
+    float li[kTopK];
+    u32x4 oi[kTopK];
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
         li[i] = lp[i * G];
-        oi[i] = w.o[(((size_t)r * kTopK + i) * G + n) * kHeadDim + d];
+        oi[i] = ld16(w.o + (((size_t)r * kTopK + i) * G + n) * kHeadDim + 8 * part);
     }
     const int npages = min(kTopK, ceil_div(row_lens[r], kBlock));
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) mx = (i < npages) ? fmaxf(mx, li[i]) : mx;
-    float den = 0.f, acc = 0.f;
+    float den = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
         const float wi = __expf(li[i] - mx);
-        den = (i < npages) ? den + wi : den;
-        acc = (i < npages) ? acc + wi * oi[i] : acc;
+        const bool ok = i < npages;
+        den = ok ? den + wi : den;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = ok ? acc[2 * e] + wi * bf16_lo(oi[i][e]) : acc[2 * e];
+            acc[2 * e + 1] = ok ? acc[2 * e + 1] + wi * bf16_hi(oi[i][e]) : acc[2 * e + 1];
+        }
     }
+    const float inv = 1.0f / den;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
     const int s = r / Hkv;
     const int h = (r % Hkv) * G + n;
-    out[((size_t)s * Hq + h) * kHeadDim + d] = f32_to_bf16(acc / den);
-    if (lse_out && d == 0) lse_out[(size_t)s * Hq + h] = mx + __logf(den);
+    *reinterpret_cast<u32x4*>(out + ((size_t)s * Hq + h) * kHeadDim + 8 * part) = o;
+    if (lse_out && part == 0) lse_out[(size_t)s * Hq + h] = mx + __logf(den);
+}
+
+hipError_t launch_merge(const MsaShape& s, const int32_t* row_lens, const void* ws, uint16_t* out,
+                        float* lse, hipStream_t st) {
+    const int R = s.B * s.Hkv;
+    const int n = R * (s.Hq / s.Hkv) * 16;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(ceil_div(n, kMergeThreads)), dim3(kMergeThreads),
+                       0, st, row_lens, ws, out, lse, s.Hq, s.Hkv, R);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -300,7 +327,7 @@ size_t msa_decode_ws_bytes(const MsaShape& s) {
     using namespace msa;
     const size_t R = (size_t)s.B * s.Hkv;
     const size_t G = (size_t)(s.Hq / s.Hkv);
-    const size_t bytes = R * kTopK * G * (kHeadDim + 1) * sizeof(float);
+    const size_t bytes = R * kTopK * G * (kHeadDim * sizeof(uint16_t) + sizeof(float));
     return (bytes + 255) / 256 * 256;
 }
 
@@ -311,15 +338,12 @@ hipError_t msa_launch_decode(const MsaShape& s, const uint16_t* q, const uint16_
     using namespace msa;
     const int R = s.B * s.Hkv;
     if (R == 0) return hipSuccess;
-    const int G = s.Hq / s.Hkv;
     const float scale_log2 = s.scale * kLog2e;
     hipLaunchKernelGGL(decode_page_kernel, dim3(kTopK, R), dim3(kDecThreads), 0, st, q, k_cache,
                        v_cache, page_table, row_lens, ws, s.Hq, s.Hkv, R, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(R * G), dim3(kHeadDim), 0, st, row_lens, ws, out,
-                       lse, s.Hq, s.Hkv, R);
-    return hipGetLastError();
+    return launch_merge(s, row_lens, ws, out, lse, st);
 }
 
 namespace {
@@ -390,7 +414,5 @@ hipError_t msa_launch_decode_step(const MsaShape& s, const uint16_t* q_idx, cons
     else e = MSA_FUSED(32, 4, false);
 #undef MSA_FUSED
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(R * (s.Hq / s.Hkv)), dim3(kHeadDim), 0, st,
-                       row_lens, ws, out, lse, s.Hq, s.Hkv, R);
-    return hipGetLastError();
+    return launch_merge(s, row_lens, ws, out, lse, st);
 }

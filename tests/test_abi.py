@@ -46,7 +46,7 @@ def dims(**kw):
 
 def test_workspace_sizes():
     d = dims()
-    assert L.msa_decode_workspace_size(d) >= 2 * 2 * 16 * 4 * 129 * 4
+    assert L.msa_decode_workspace_size(d) >= 2 * 2 * 16 * 4 * (128 * 2 + 4)
     assert L.msa_decode_workspace_size(d) % 256 == 0
     assert L.msa_prefill_workspace_size(d, 100) > 100 * 8 * 16 * 128 * 2
     assert L.msa_decode_workspace_size(dims(head_dim=64)) == 0

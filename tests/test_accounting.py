@@ -67,11 +67,45 @@ def test_traffic_record_scales_the_counters_by_the_copy(tmp_path):
     _counter_csv(p["w"], [(score, "WRITE_SIZE", 10.0), (other, "WRITE_SIZE", 7777.0)])
     src = tmp_path / "k.hip"
     src.write_bytes(b"kernel source")
-    rec = bench.traffic_record(p["cf"], p["cw"], p["f"], p["w"], str(src))
+    rec = bench.traffic_record("index_score", p["cf"], p["cw"], p["f"], p["w"], [str(src)])
     assert rec["copy_calibration"]["fetch_factor"] == 2.0
     assert rec["copy_calibration"]["write_factor"] == 1.0
-    assert rec["launches"] == {"fetch_pass": 2, "write_pass": 1}
+    assert rec["kernels"][0]["launches"] == {"fetch_pass": 2, "write_pass": 1}
     assert rec["fetch_bytes_per_launch"] == 101 * 1024 * 2
     assert rec["write_bytes_per_launch"] == 10 * 1024
     assert rec["source_sha256"] == hashlib.sha256(b"kernel source").hexdigest()
     assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(gen.config(2))
+
+
+def test_decode_step_traffic_record_sums_its_three_kernels(tmp_path):
+    """The decode-step record sums the per-launch means of the step's three
+    kernels (one launch each per layer-step), ignores the ABI scoring form and
+    other kernels, and hashes every source in order."""
+    import hashlib
+    import bench
+    ns = "void msa::(anonymous namespace)::"
+    step_score = ns + "index_score_kernel<false, false>(unsigned short const*)"
+    abi_score = ns + "index_score_kernel<true, false>(unsigned short const*)"
+    fused = ns + "decode_fused_kernel<8, 1, true>(float const*)"
+    merge = ns + "decode_merge_kernel(int const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    p = {k: str(tmp_path / f"{k}.csv") for k in ("cf", "cw", "f", "w")}
+    _counter_csv(p["cf"], [(copy, "FETCH_SIZE", 131072.0)])
+    _counter_csv(p["cw"], [(copy, "WRITE_SIZE", 262144.0)])
+    _counter_csv(p["f"], [(step_score, "FETCH_SIZE", 30.0), (fused, "FETCH_SIZE", 40.0),
+                          (fused, "FETCH_SIZE", 42.0), (merge, "FETCH_SIZE", 2.0),
+                          (abi_score, "FETCH_SIZE", 5000.0)])
+    _counter_csv(p["w"], [(step_score, "WRITE_SIZE", 1.0), (fused, "WRITE_SIZE", 3.0),
+                          (merge, "WRITE_SIZE", 0.5)])
+    srcs = []
+    for i in range(2):
+        f = tmp_path / f"s{i}.hip"
+        f.write_bytes(b"part %d" % i)
+        srcs.append(str(f))
+    rec = bench.traffic_record("decode_step", p["cf"], p["cw"], p["f"], p["w"], srcs)
+    assert [k["fetch_size_kib_per_launch"] for k in rec["kernels"]] == [30.0, 41.0, 2.0]
+    assert rec["fetch_bytes_per_launch"] == (30 + 41 + 2) * 1024 * 2
+    assert rec["write_bytes_per_launch"] == int((1 + 3 + 0.5) * 1024)
+    assert rec["source_sha256"] == hashlib.sha256(b"part 0part 1").hexdigest()
+    cfg = gen.config(2)
+    assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
