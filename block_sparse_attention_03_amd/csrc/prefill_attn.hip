@@ -510,7 +510,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     }
     __syncthreads();
 
-    const int wave = tid / kWave;
+    // wave-uniform to the compiler too, so the tile loop's exits are scalar
+    // branches and its load waits stay exact across iterations
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int n = lane % 32;   // result column = row of this lane
     const int h = lane / 32;   // lane half
@@ -550,29 +552,37 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // never the previous tile's stores.
     int tile = wave;
     if (tile * 32 >= nrows) return;  // wavefront-uniform; no workgroup barrier follows
-    int t = 0, head = 0, slot = 0;
-    bool row_ok = row_info(tile, entry_of(tile), &t, &head, &slot);
-    int entry_next = entry_of(tile + kWaves);
-    u32x4 qraw[8];
-    gather_q(t, head, qraw);
-    // wait for the first tile's loads here, so that at the loop head neither
-    // path has its query rows in flight and no wait there reaches the
+    // Query rows are gathered two tiles ahead into two register buffers used
+    // in turn, so that while a tile computes the gathers of this wavefront's
+    // next two tiles are in flight (the kernel's rate is set by the bytes it
+    // keeps in flight: one workgroup per compute unit).
+    int tA = 0, hA = 0, sA = 0, tB = 0, hB = 0, sB = 0;
+    bool okA = row_info(tile, entry_of(tile), &tA, &hA, &sA);
+    bool okB = row_info(tile + kWaves, entry_of(tile + kWaves), &tB, &hB, &sB);
+    int entry_next = entry_of(tile + 2 * kWaves);
+    u32x4 qA[8], qB[8];
+    gather_q(tA, hA, qA);
+    gather_q(tB, hB, qB);
+    // wait for the first two tiles' loads here, so that at the loop head
+    // neither path has its query rows in flight and no wait there reaches the
     // previous tile's stores (s_waitcnt immediate: vmcnt 0, other counters
     // unconstrained)
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    for (; tile * 32 < nrows; tile += kWaves) {
+    auto step = [&](u32x4 (&qraw)[8], int& t, int& head, int& slot, bool& row_ok) {
         // B operands (k-step i of lane half h: dims 64h + 8i .. +7)
         bf16x8 qb[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) qb[i] = as_bf16x8(qraw[i]);
         const int cur_t = t, cur_slot = slot, cur_head = head;
         const bool cur_ok = row_ok;
-        // next tile's rows are gathered while this one computes
-        const int next = tile + kWaves;
-        row_ok = row_info(next, entry_next, &t, &head, &slot);
-        gather_q(t, head, qraw);
-        entry_next = entry_of(next + kWaves);
+        // The rows two tiles ahead go into this buffer once this tile's
+        // S^T products have read it (so the old and new rows never share
+        // the registers' lifetime).  The entry of the tile after those is
+        // loaded first: the next step needs it before its own gather, and
+        // waits count loads in issue order.
+        const int ahead = tile + 2 * kWaves;
+        const int entry_after = entry_of(ahead + kWaves);
 
         // S^T = K Q^T: tile mt = tokens 32mt..32mt+31; value v of the lane is
         // token 32mt + 8(v/4) + 4h + v%4 of row n.  Operands of token tile
@@ -597,6 +607,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
             // keep the scheduler from hoisting further tiles' operand reads
             __builtin_amdgcn_sched_barrier(0);
         }
+        row_ok = row_info(ahead, entry_next, &t, &head, &slot);
+        gather_q(t, head, qraw);
+        entry_next = entry_after;
 
         // causal cut inside the query's own block
         const int lim = pos0 + cur_t - tok0;  // token index (within block) must be <= lim
@@ -695,7 +708,17 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                                          : w.trash_lse + lane;
         *ldst = mx * scale_log2 * kLn2 + __logf(sum);
         __builtin_amdgcn_wave_barrier();
+        };
+    // whole pairs of this wavefront's tiles, then an odd last one: a loop with
+    // no exit between its two steps, so that each step's wait is exact
+    const int mine = (ceil_div(nrows, 32) - wave + kWaves - 1) / kWaves;  // >= 1
+    for (int pair = 0; pair < mine / 2; ++pair) {
+        step(qA, tA, hA, sA, okA);
+        tile += kWaves;
+        step(qB, tB, hB, sB, okB);
+        tile += kWaves;
     }
+    if (mine & 1) step(qA, tA, hA, sA, okA);
 }
 
 // Small buckets (at most kSmallRows (query, head) rows): one 256-thread
