@@ -495,6 +495,8 @@ def measured_ceilings():
     c.msa_calib_read_grid.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     c.msa_calib_read_sink_len.restype = ctypes.c_size_t
+    c.msa_calib_copy_grid.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_void_p]
     c.msa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     c.msa_calib_mfma_flop.restype = ctypes.c_double
     c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -522,6 +524,16 @@ def measured_ceilings():
         fns = [lambda i=i, g=grid: read(base + i * small, small, g) for i in range(nbytes // small)]
         ms = time_calls(fns, 2 * len(fns), len(fns))
         sized[grid] = small / (ms * 1e-3) / 1e9
+    # a device copy of 800 MiB (1.6 GiB of traffic, half reads and half
+    # writes: the mix and size of the prefill block-major kernel's traffic)
+    half = 800 << 20
+    copy = {}
+    for grid in (1024, 2048, 4096):
+        def cp(g=grid):
+            if c.msa_calib_copy_grid(base, base + half, half, g, st) != 0:
+                raise RuntimeError("msa_calib_copy_grid failed")
+        ms = time_calls([cp], 6, 2)
+        copy[grid] = 2 * half / (ms * 1e-3) / 1e9
     tflops = {}
     for blocks in (1024, 2048):
         # enough warm-up launches (about 1 ms each) for the clocks to settle
@@ -530,11 +542,14 @@ def measured_ceilings():
     del buf
     torch.cuda.empty_cache()
     gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
+    gc = max(copy, key=copy.get)
     return {"hbm_read_gbs": round(big[gb], 1),
             "hbm_read_64mib_gbs": round(sized[gs], 1),
+            "hbm_copy_800mib_gbs": round(copy[gc], 1),
             "mfma_bf16_tflops": round(tflops[bm], 1),
             "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
-                   f"and of 64 MiB slices back to back (best grid {gs}); 32x32x16 bf16 MFMA "
+                   f"and of 64 MiB slices back to back (best grid {gs}); a device copy of 800 MiB "
+                   f"(read + write bytes, best grid {gc}); 32x32x16 bf16 MFMA "
                    f"loop, 4 independent chains per wave, {bm // 256 * 4} waves per CU",
             "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
             "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
@@ -751,6 +766,13 @@ def main():
             "sparse_attn_call_ms": round(attn3, 4),
             "sparse_attn_call_mfma_frac": round(tf(fl_attn, attn3) / acc.BF16_PEAK_TFLOPS, 4),
             "sparse_attn_call_mfma_frac_of_measured": round(tf(fl_attn, attn3) / ceil["mfma_bf16_tflops"], 4),
+            # the call's own traffic: K/V once, query rows gathered per
+            # (query, head, slot), partials written and read back, outputs
+            "sparse_attn_call_traffic": {
+                "algorithmic_bytes": acc.prefill_attn_bytes(c3),
+                "achieved_gbs": round(acc.prefill_attn_bytes(c3) / (attn3 * 1e-3) / 1e9, 1),
+                "frac_of_copy_ceiling": round(acc.prefill_attn_bytes(c3) / (attn3 * 1e-3) / 1e9
+                                              / ceil["hbm_copy_800mib_gbs"], 4)},
             "index_score_ms": round(score3, 4),
             "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
             "index_score_mfma_frac_of_measured": round(tf(fl_score, score3) / ceil["mfma_bf16_tflops"], 4),

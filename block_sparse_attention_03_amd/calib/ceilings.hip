@@ -1,5 +1,6 @@
 // ceilings.hip -- measured ceilings for the roofline fractions: a streaming
-// HBM read and a bf16 matrix-core loop on MI355X (gfx950).  Not part of the
+// HBM read, a device copy (reads and writes at once) and a bf16 matrix-core
+// loop on MI355X (gfx950).  Not part of the
 // MSA library: the benchmark loads this separate libmsa_calib.so to report
 // achieved bandwidth and FLOP rate against what the chip actually sustains,
 // next to the published peaks.
@@ -35,6 +36,22 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
     sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+// dst = src, 16-byte chunks with streaming loads, eight in flight per thread:
+// the rate of traffic that is half reads and half writes.
+__global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dst[i + u * stride] = v[u];
+    }
+    for (; i < n16; i += stride) dst[i] = __builtin_nontemporal_load(src + i);
 }
 
 // Four independent chains of 32x32x16 bf16 products per wavefront, iters
@@ -88,6 +105,20 @@ int msa_calib_read_grid(const void* buf, size_t bytes, int blocks, uint32_t* sin
     hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), bytes / 16,
                        sink);
+    return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16) from src to dst (not overlapping) with
+// `blocks` workgroups (1 .. msa_calib_read_blocks()).
+int msa_calib_copy_grid(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+    if (!src || !dst || bytes % 16 != 0 || blocks <= 0 || blocks > msa_calib_read_blocks())
+        return (int)hipErrorInvalidValue;
+    const char* a = static_cast<const char*>(src);
+    const char* b = static_cast<const char*>(dst);
+    if (a < b + bytes && b < a + bytes) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), bytes / 16);
     return (int)hipGetLastError();
 }
 

@@ -36,14 +36,48 @@ __device__ __forceinline__ DecodeWs decode_ws(void* ws, int R, int G) {
     return w;
 }
 
-// The G query heads of row r (sequence s, group g) against one page holding
+// Q of row (sequence s, group g) as matrix-core B operands: head n of the
+// group in column n (zero beyond G), dims 32i + 8kg .. +7 at k-step i.
+__device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q, int s, int g, int G,
+                                                int Hq, bf16x8 (&qb)[4]) {
+    const int lane = threadIdx.x % kWave;
+    const int n = lane % 16;
+    const int kg = lane / 16;
+    const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
+}
+
+// One page's K and V in registers: K of this wavefront's 32 tokens as
+// contiguous rows (operand order comes later, through the V tile), V rows
+// with coalesced 16-byte loads (16 lanes per 256-byte row).  The whole page
+// is loaded -- a page is always allocated in full, and unconditional loads
+// keep the compiler from waiting on them early -- and tokens at or past the
+// valid count are zeroed when V is written to LDS, so that P = 0 there never
+// meets a non-finite V.
+struct PageRegs {
+    u32x4 k[8];
+    u32x4 v[8];
+};
+
+__device__ __forceinline__ void load_page(const uint16_t* __restrict__ kp,
+                                          const uint16_t* __restrict__ vp, PageRegs& pr) {
+    const int tid = threadIdx.x;
+    load_k_rows(kp, tid / kWave, tid % kWave, pr.k);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+        pr.v[it] = ld16_stream(vp + (tid / 16 + 16 * it) * kHeadDim + 8 * (tid % 16));
+}
+
+// The G query heads of row r (operands qb) against one page (in pr) holding
 // nv valid tokens: writes the normalised partial output and log-sum-exp of
-// page slot `slot`.  Every thread of the 256-thread workgroup calls it.
-__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
-                                            const uint16_t* __restrict__ kp,
-                                            const uint16_t* __restrict__ vp, int nv, int s, int g,
-                                            int G, int Hq, int r, int slot, void* __restrict__ ws,
-                                            int R, float scale_log2, DecodeShared& sh) {
+// page slot `slot`.  Every thread of the 256-thread workgroup calls it; the
+// page's K goes through the V tile first, so a caller that attends another
+// page with the same tile puts a barrier between the two.
+__device__ __forceinline__ void compute_page(const bf16x8 (&qb)[4], const PageRegs& pr, int nv,
+                                             int G, int r, int slot, void* __restrict__ ws, int R,
+                                             float scale_log2, DecodeShared& sh) {
     uint16_t* vs = sh.vs;
     uint16_t* pl = sh.pl;
     auto& red_max = sh.red_max;
@@ -53,32 +87,8 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
     const int lane = tid % kWave;
     const int n = lane % 16;   // head column (B / result) or row of A
     const int kg = lane / 16;  // lane group
-
-    // Loads in the order their data is needed -- Q, this wavefront's K, then
-    // V -- since vector loads retire in issue order: the scores and the
-    // softmax below wait only for Q and K while V is still arriving.
-    bf16x8 qb[4];  // head n of this group, zero beyond G
-    {
-        const uint16_t* qrow = q + ((size_t)s * Hq + g * G + n) * kHeadDim;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            qb[i] = as_bf16x8(n < G ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
-    }
-    // K of this wave's 32 tokens: contiguous loads, then operand order
-    // through this wave's quarter of the V tile
-    u32x4 kraw[8];
-    load_k_rows(kp, wave, lane, kraw);
-    // V rows with coalesced 16-byte loads (16 lanes per 256-byte row).  The
-    // whole page is loaded -- a page is always allocated in full, and
-    // unconditional loads keep the compiler from waiting on them early --
-    // and tokens at or past nv are zeroed when V is written to LDS, so that
-    // P = 0 there never meets a non-finite V.
-    u32x4 vv[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-        vv[it] = ld16_stream(vp + (tid / 16 + 16 * it) * kHeadDim + 8 * (tid % 16));
-    // keep every load issued here, ahead of the first wait
-    __builtin_amdgcn_sched_barrier(0);
+    const u32x4 (&kraw)[8] = pr.k;
+    const u32x4 (&vv)[8] = pr.v;
     bf16x8 ka[2][4];
     k_rows_to_operands(kraw, wave, lane, vs, ka);
     {
@@ -172,6 +182,23 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
 }
 
 
+// Q, the page's K, then its V -- loads in the order their data is needed,
+// since vector loads retire in issue order: the scores and the softmax wait
+// only for Q and K while V is still arriving -- then the page's attention.
+__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ kp,
+                                            const uint16_t* __restrict__ vp, int nv, int s, int g,
+                                            int G, int Hq, int r, int slot, void* __restrict__ ws,
+                                            int R, float scale_log2, DecodeShared& sh) {
+    bf16x8 qb[4];
+    load_q_operands(q, s, g, G, Hq, qb);
+    PageRegs pr;
+    load_page(kp, vp, pr);
+    // keep every load issued here, ahead of the first wait
+    __builtin_amdgcn_sched_barrier(0);
+    compute_page(qb, pr, nv, G, r, slot, ws, R, scale_log2, sh);
+}
+
 __global__ __launch_bounds__(kDecThreads)
 void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
@@ -254,6 +281,85 @@ void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
     const size_t page_off = ((size_t)pg * Hkv + g) * kBlock * kHeadDim;
     attend_page(q, k_cache + page_off, v_cache + page_off, nv, s, g, Hq / Hkv, Hq, r, slot, ws, R,
                 scale_log2, sh);
+}
+
+// Fused decode for batches with more page workgroups than the chip holds at
+// once: the workgroup of (row r, slots PPW*x .. PPW*x + PPW-1) makes the
+// row's selection once, as decode_fused_kernel does, keeps the row's query
+// operands, and attends its pages one after the other with the next page's
+// K and V loads issued before the current page's products, so that each
+// compute unit keeps a page in flight while it computes.  Each page leaves
+// the same partial output and log-sum-exp as in decode_fused_kernel, for the
+// same merge.
+template <int NPT, int W, bool PAGES, int PPW>
+__global__ __launch_bounds__(kDecThreads)
+void decode_multi_kernel(const float* __restrict__ scores,     // [B, Hkv, maxblk]
+                         const int32_t* __restrict__ block_table,
+                         const int32_t* __restrict__ seq_lens,
+                         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                         const uint16_t* __restrict__ v_cache, int32_t* __restrict__ row_lens,
+                         int32_t* __restrict__ sel_out, void* __restrict__ ws, int Hq, int Hkv,
+                         int R, int maxblk, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    __shared__ int32_t sel_idx[kTopK];
+    __shared__ int32_t sel_page[kTopK];
+    static_assert(sizeof(SelectShared<W>) <= sizeof(sh.vs), "selection scratch");
+    SelectShared<W>* ssh = reinterpret_cast<SelectShared<W>*>(sh.vs);
+    const int slot0 = blockIdx.x * PPW;
+    const int r = blockIdx.y;
+    const int s = r / Hkv;
+    const int g = r % Hkv;
+    const int G = Hq / Hkv;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int w = (W == 1) ? 0 : wave;
+    const bool selecting = (W == 4 || wave == 0);
+    float raw[NPT];
+    int page[NPT];
+    if (selecting)
+        load_candidates<NPT, W, PAGES>(scores + (size_t)r * maxblk, block_table + (size_t)s * maxblk,
+                                       maxblk, w, lane, raw, page);
+    const int p = seq_lens[s] - 1;
+    const int b_loc = p / kBlock;
+    const int n_sel = min(kTopK, b_loc + 1);
+    if (selecting)
+        select_row<NPT, W>(raw, page, b_loc, w, lane, ssh, [&](int pos, uint32_t, int b, int pg) {
+            sel_idx[pos] = b;
+            sel_page[pos] = pg;
+        });
+    __syncthreads();
+    if (slot0 >= n_sel) return;  // uniform
+    if (slot0 == 0) {
+        if (threadIdx.x < kTopK && sel_out) sel_out[(size_t)r * kTopK + threadIdx.x] = sel_idx[threadIdx.x];
+        if (threadIdx.x == 0) row_lens[r] = (n_sel - 1) * kBlock + (p - kBlock * b_loc + 1);
+    }
+    // pages of this workgroup, wave-uniform to the compiler (scalar loop
+    // control, exact load waits across the loop)
+    const int npg = __builtin_amdgcn_readfirstlane(min(PPW, n_sel - slot0));
+    auto page_ptr = [&](int slot, const uint16_t* cache) {
+        const int pg = PAGES ? sel_page[slot] : block_table[(size_t)s * maxblk + sel_idx[slot]];
+        return cache + ((size_t)pg * Hkv + g) * kBlock * kHeadDim;
+    };
+    // ascending order puts the own (partial) block last
+    auto valid = [&](int slot) { return (slot == n_sel - 1) ? p - kBlock * b_loc + 1 : kBlock; };
+    bf16x8 qb[4];
+    load_q_operands(q, s, g, G, Hq, qb);
+    PageRegs pa, pb;
+    load_page(page_ptr(slot0, k_cache), page_ptr(slot0, v_cache), pa);
+    // pairs of pages through two register sets, then an odd last page
+    for (int k = 0; k + 1 < npg; k += 2) {
+        load_page(page_ptr(slot0 + k + 1, k_cache), page_ptr(slot0 + k + 1, v_cache), pb);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_page(qb, pa, valid(slot0 + k), G, r, slot0 + k, ws, R, scale_log2, sh);
+        __syncthreads();  // this page's reads of the V tile are done
+        if (k + 2 < npg)
+            load_page(page_ptr(slot0 + k + 2, k_cache), page_ptr(slot0 + k + 2, v_cache), pa);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_page(qb, pb, valid(slot0 + k + 1), G, r, slot0 + k + 1, ws, R, scale_log2, sh);
+        __syncthreads();
+    }
+    if (npg & 1) compute_page(qb, pa, valid(slot0 + npg - 1), G, r, slot0 + npg - 1, ws, R,
+                              scale_log2, sh);
 }
 
 // Log-Sum-Exp merge of a row's pages: 16 threads per (row, head), each
@@ -364,6 +470,11 @@ size_t msa_decode_step_ws_bytes(const MsaShape& s) {
     return bytes;
 }
 
+// Compute units, and the page workgroups the chip holds at once (LDS for four
+// of 37.6 KB each per compute unit).
+constexpr int kComputeUnits = 256;
+constexpr int kResidentPageWorkgroups = kComputeUnits * 4;
+
 template <int NPT, int W, bool PAGES>
 static hipError_t launch_fused(const MsaShape& s, const float* scores, const int32_t* block_table,
                                const int32_t* seq_lens, const uint16_t* q, const uint16_t* k_cache,
@@ -371,9 +482,22 @@ static hipError_t launch_fused(const MsaShape& s, const float* scores, const int
                                void* ws, hipStream_t st) {
     using namespace msa;
     const int R = s.B * s.Hkv;
-    hipLaunchKernelGGL((decode_fused_kernel<NPT, W, PAGES>), dim3(kTopK, R), dim3(kDecThreads), 0, st,
-                       scores, block_table, seq_lens, q, k_cache, v_cache, row_lens, sel_out, ws,
-                       s.Hq, s.Hkv, R, s.maxblk, s.scale * kLog2e);
+#define MSA_MULTI(PPW)                                                                           \
+    hipLaunchKernelGGL((decode_multi_kernel<NPT, W, PAGES, PPW>), dim3(kTopK / PPW, R),              \
+                       dim3(kDecThreads), 0, st, scores, block_table, seq_lens, q, k_cache, v_cache, \
+                       row_lens, sel_out, ws, s.Hq, s.Hkv, R, s.maxblk, s.scale * kLog2e)
+    // One page per workgroup while every page workgroup fits on the chip at
+    // once; past that, several slots per workgroup (one selection each), as
+    // many as still leave two workgroups per compute unit.
+    if (R * kTopK >= 8 * 2 * kComputeUnits) MSA_MULTI(8);
+    else if (R * kTopK >= 4 * 2 * kComputeUnits) MSA_MULTI(4);
+    else if (R * kTopK > kResidentPageWorkgroups) MSA_MULTI(2);
+#undef MSA_MULTI
+    else
+        hipLaunchKernelGGL((decode_fused_kernel<NPT, W, PAGES>), dim3(kTopK, R),
+                           dim3(kDecThreads), 0, st, scores, block_table, seq_lens, q, k_cache,
+                           v_cache, row_lens, sel_out, ws, s.Hq, s.Hkv, R, s.maxblk,
+                           s.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -187,7 +187,8 @@ def test_calibration_library_exports():
     path = os.path.join(os.path.dirname(L.LIB_PATH), "libmsa_calib.so")
     c = ctypes.CDLL(path)
     for name in ("msa_calib_read_blocks", "msa_calib_read_sink_len", "msa_calib_read",
-                 "msa_calib_read_grid", "msa_calib_mfma_flop", "msa_calib_mfma"):
+                 "msa_calib_read_grid", "msa_calib_copy_grid", "msa_calib_mfma_flop",
+                 "msa_calib_mfma"):
         assert hasattr(c, name), name
     c.msa_calib_mfma_flop.restype = ctypes.c_double
     c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -196,6 +197,10 @@ def test_calibration_library_exports():
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     # argument errors are caught before any launch
     assert c.msa_calib_read_grid(None, 16, 4, None, 0, None) != 0
+    c.msa_calib_copy_grid.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_int, ctypes.c_void_p]
+    assert c.msa_calib_copy_grid(None, P(0x1000), 16, 4, None) != 0
+    assert c.msa_calib_copy_grid(P(0x1000), P(0x1010), 32, 4, None) != 0  # overlapping
 
 
 def test_validate_inputs_errors():

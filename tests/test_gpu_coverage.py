@@ -17,6 +17,12 @@ wide form with most of its candidate slots empty.  The cases here put a long
 and a short row in each band; each goes through the four calls (checked
 against the oracle, padding poisoned with NaN) and through msa_decode_step
 (bit-equal to the four calls).
+
+msa_decode_step also picks, by the number of flattened rows R (sequences x
+KV groups), how many page slots one workgroup attends: one while all 16 R
+page workgroups fit on the chip at once (R <= 64), else 2, 4 or 8
+(decode_multi_kernel<NPT, W, PAGES, slots>: R < 128, R < 256, R >= 256).
+MULTI covers each of those with short and long rows.
 """
 import numpy as np
 import pytest
@@ -95,3 +101,42 @@ def test_prefill_row_with_no_selection():
     assert (err <= parity.OUT_ATOL + parity.OUT_RTOL * np.abs(ref_o[ok])).all()
     assert np.abs(got_l[ok] - ref_l[ok]).max() <= parity.LSE_ATOL
 
+
+def _lens(n, lo, hi, seed):
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(lo, hi, size=n)]
+
+
+MULTI = [
+    # 96 rows: two slots per workgroup, one selecting wavefront
+    gen.MsaConfig("multi_96_rows", _lens(12, 1_000, 40_000, 1), [1] * 12, 48, 8,
+                  permute_pages=True, seed=94),
+    # 72 rows with one 600,000-token row: two slots, four selecting
+    # wavefronts without block-table loads (width 4688)
+    gen.MsaConfig("multi_72_rows_600k", [600_000] + _lens(8, 500, 9_000, 2), [1] * 9, 16, 8,
+                  permute_pages=True, seed=95),
+    # 144 rows with a 300,000-token row: four slots, four selecting
+    # wavefronts (width 2344)
+    gen.MsaConfig("multi_144_rows_300k", [300_000] + _lens(17, 200, 12_000, 3), [1] * 18, 24, 8,
+                  permute_pages=True, seed=96),
+    # 256 rows: eight slots per workgroup
+    gen.MsaConfig("multi_256_rows", _lens(32, 3_000, 20_000, 4), [1] * 32, 32, 8,
+                  permute_pages=True, seed=97),
+]
+
+
+@pytest.mark.parametrize("cfg", MULTI, ids=lambda c: c.name)
+def test_multi_page_workgroups(cfg):
+    """Several page slots per workgroup in msa_decode_step: the four calls
+    against the oracle, and the step bit-equal to them."""
+    R = cfg.num_seqs * cfg.num_kv_heads
+    print(f"[multi] {cfg.name} rows={R} maxblk={cfg.max_blocks}", flush=True)
+    assert R * cfg.topk > 1024
+    x, step = parity.full_check(cfg, poison=True, attn_rows=1024)
+    fused = MsaStep(x, fused=True)
+    fused.sel.fill_(-7)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.sel, step.sel)
+    assert torch.equal(fused.out, step.out)
+    assert torch.equal(fused.lse, step.lse)

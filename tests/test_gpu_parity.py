@@ -282,8 +282,8 @@ def test_graph_replay_matches_eager(prefill):
     gen.MsaConfig("fused_hidx", [7000, 300], [1, 1], 12, 3, num_idx_heads=3, permute_pages=True,
                   seed=43),
     gen.config(2), gen.config(5), gen.config(4),
-    # 160 and 320 rows: each page workgroup of the fused step attends 4 or 8
-    # of its row's slots
+    # 160 and 320 rows (more page workgroups than the chip holds at once):
+    # each page workgroup of the fused step attends two of its row's slots
     gen.MsaConfig("fused_160_rows", [(37 * i * i) % 20000 + 150 for i in range(20)], [1] * 20,
                   16, 8, permute_pages=True, seed=57),
     gen.MsaConfig("fused_320_rows", [(53 * i * i) % 9000 + 2100 for i in range(40)], [1] * 40,
