@@ -25,13 +25,16 @@ def test_noalloc_decode_step_equals_the_workspace_form():
     """Calls in a row on one GPU's scratch: the 8 x 60,000 paged decode, then a
     smaller ragged batch, then rows past 8192 blocks (whose selection and page
     table also live in the scratch, with and without the selection output),
+    then the 16-sequence ragged decode (several page slots per workgroup),
     then the first shape again.  Each equals msa_decode_step with its own
     workspace, bit for bit (out, lse, selection)."""
     cases = [gen.config(2),
              gen.MsaConfig("noalloc_small", [300, 1000, 4500], [1, 1, 1], 12, 3,
                            permute_pages=True, seed=91),
              gen.MsaConfig("noalloc_8300_blocks", [8300 * 128 - 5, 3000], [1, 1], 2, 1,
-                           permute_pages=True, seed=92)]
+                           permute_pages=True, seed=92),
+             # 128 flattened rows: several page slots per workgroup
+             gen.config(5)]
     steps = []
     for cfg in cases:
         assert L.msa_decode_step_workspace_size(L.dims_for(cfg)) <= L.MSA_STATIC_SCRATCH_BYTES
@@ -40,7 +43,7 @@ def test_noalloc_decode_step_equals_the_workspace_form():
         ref.run()
         steps.append(ref)
     torch.cuda.synchronize()
-    for i, k in enumerate([0, 1, 2, 0]):
+    for i, k in enumerate([0, 1, 2, 3, 0]):
         ref = steps[k]
         print(f"[noalloc] call {i}: {cases[k].name}", flush=True)
         out, lse, sel = _noalloc_into(ref)
