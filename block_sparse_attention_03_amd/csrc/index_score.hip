@@ -62,7 +62,8 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
                         const int32_t* __restrict__ cu_q,
                         float* __restrict__ scores,           // [T, Hkv, maxblk]
                         int Hkv, int Hidx, int maxblk, AppendRows ap) {
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform to the compiler too: the block's tests are scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     // grid: x = (sequence, index head), y = block chunk, so the sequences vary
     // fastest in dispatch order; the pair is skewed by the chunk because
@@ -76,9 +77,12 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     const int ih = xs % Hidx;
     if (b >= maxblk) return;
 
-    // the block-table entry (in bounds for any b < maxblk) is read beside the
-    // sequence length rather than after it
-    const int page = block_table[(size_t)s * maxblk + b];
+    // The block-table entry is loaded only once the block is known to be
+    // visible: in a ragged batch most of the grid, which is sized by the
+    // longest row, holds blocks past their sequence's end, and a wavefront
+    // that has issued a load keeps its slot until the load returns.  The
+    // sequence length, which decides, is a scalar load (cached after its
+    // first use).
     const int L = seq_lens[s];
     // cu_q == nullptr: decode, query token s is sequence s's only query
     const int q0 = cu_q ? cu_q[s] : s;
@@ -107,6 +111,7 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
         }
         return;
     }
+    const int page = block_table[(size_t)s * maxblk + b];  // b < maxblk: in bounds
 
     // A operands: the block's index keys.  Tile mt covers tokens 16*mt..16*mt+15;
     // k-step i of lane group kg takes dims 32*i + 8*kg .. +7 (16-byte chunk
