@@ -534,6 +534,16 @@ def measured_ceilings():
                 raise RuntimeError("msa_calib_copy_grid failed")
         ms = time_calls([cp], 6, 2)
         copy[grid] = 2 * half / (ms * 1e-3) / 1e9
+    # the same copy of 96 MiB each way, a footprint the 256 MB Infinity Cache
+    # holds: what keeping a round trip's data in that cache could gain
+    small_half = 96 << 20
+    copy_small = {}
+    for grid in (1024, 2048, 4096):
+        def cps(g=grid):
+            if c.msa_calib_copy_grid(base, base + small_half, small_half, g, st) != 0:
+                raise RuntimeError("msa_calib_copy_grid failed")
+        ms = time_calls([cps], 40, 8)
+        copy_small[grid] = 2 * small_half / (ms * 1e-3) / 1e9
     tflops = {}
     for blocks in (1024, 2048):
         # enough warm-up launches (about 1 ms each) for the clocks to settle
@@ -543,13 +553,15 @@ def measured_ceilings():
     torch.cuda.empty_cache()
     gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
     gc = max(copy, key=copy.get)
+    gcs = max(copy_small, key=copy_small.get)
     return {"hbm_read_gbs": round(big[gb], 1),
             "hbm_read_64mib_gbs": round(sized[gs], 1),
             "hbm_copy_800mib_gbs": round(copy[gc], 1),
+            "copy_96mib_gbs": round(copy_small[gcs], 1),
             "mfma_bf16_tflops": round(tflops[bm], 1),
             "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
                    f"and of 64 MiB slices back to back (best grid {gs}); a device copy of 800 MiB "
-                   f"(read + write bytes, best grid {gc}); 32x32x16 bf16 MFMA "
+                   f"(read + write bytes, best grid {gc}) and of 96 MiB (best grid {gcs}); 32x32x16 bf16 MFMA "
                    f"loop, 4 independent chains per wave, {bm // 256 * 4} waves per CU",
             "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
             "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
