@@ -61,6 +61,10 @@ def parse():
                     help="only run the headline's msa_decode_step layer-steps (PMC passes)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run chunked-prefill layer-steps, 8192 tokens on 57,344 (PMC passes)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only run the bf16 rate probes (constant-operand MFMA loop, vendor GEMM "
+                         "8192^3 on N(0,1) and on constant operands) and the 8k chunk's scoring "
+                         "GEMM (PMC passes: clocks and matrix-core busy cycles)")
     ap.add_argument("--record-traffic", nargs=5,
                     metavar=("RECORD", "COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                     help="write traffic record RECORD (index_score: --score-only passes; "
@@ -551,6 +555,7 @@ def measured_ceilings():
         tflops[blocks] = c.msa_calib_mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
+    vendor = vendor_gemm_tflops()
     gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
     gc = max(copy, key=copy.get)
     gcs = max(copy_small, key=copy_small.get)
@@ -559,12 +564,39 @@ def measured_ceilings():
             "hbm_copy_800mib_gbs": round(copy[gc], 1),
             "copy_96mib_gbs": round(copy_small[gcs], 1),
             "mfma_bf16_tflops": round(tflops[bm], 1),
+            "vendor_gemm_bf16_randn_tflops": round(vendor["randn"], 1),
+            "vendor_gemm_bf16_const_tflops": round(vendor["const"], 1),
             "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
                    f"and of 64 MiB slices back to back (best grid {gs}); a device copy of 800 MiB "
                    f"(read + write bytes, best grid {gc}) and of 96 MiB (best grid {gcs}); 32x32x16 bf16 MFMA "
-                   f"loop, 4 independent chains per wave, {bm // 256 * 4} waves per CU",
+                   f"loop on constant operands, 4 independent chains per wave, {bm // 256 * 4} waves "
+                   f"per CU; torch.matmul (hipBLASLt) bf16 8192^3 on N(0,1) and on all-ones operands",
             "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
             "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
+
+
+def vendor_gemm_tflops():
+    """bf16 rate of the vendor library's GEMM (torch.matmul, hipBLASLt) at
+    8192^3, on N(0,1) operands and on all-ones operands.  The matrix cores'
+    clock drops under random data, which the constant-operand loop does not
+    show: the random-operand rate is what a GEMM on this data can sustain."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    out = {}
+    for kind in ("randn", "const"):
+        if kind == "randn":
+            a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16, generator=g)
+        else:
+            a = torch.ones(8192, 8192, device="cuda", dtype=torch.bfloat16)
+            b = torch.ones(8192, 8192, device="cuda", dtype=torch.bfloat16)
+        c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+        ms = time_calls([lambda: torch.matmul(a, b, out=c)], 10, 5)
+        out[kind] = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def roofline_entry(name, nbytes, ms, traffic=None):
@@ -601,6 +633,17 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": a.numel() * 4, "launches": 4}))
+        return
+    if args.gemm_probe:
+        ceil = measured_ceilings()
+        cfg = gen.config(3)
+        st3 = [MsaStep(x) for x in make_layers(cfg, 2)]
+        ms = time_calls([s_.score for s_ in st3], args.steps, args.warmup)
+        print(json.dumps({"index_score_gemm_ms": ms,
+                          "index_score_gemm_tflops": acc.score_flops(cfg) / (ms * 1e-3) / 1e12,
+                          "mfma_bf16_tflops": ceil["mfma_bf16_tflops"],
+                          "vendor_gemm_bf16_randn_tflops": ceil["vendor_gemm_bf16_randn_tflops"],
+                          "vendor_gemm_bf16_const_tflops": ceil["vendor_gemm_bf16_const_tflops"]}))
         return
     if args.prefill_only:
         cfg = gen.config(3)
@@ -788,6 +831,8 @@ def main():
             "index_score_ms": round(score3, 4),
             "index_score_mfma_frac": round(tf(fl_score, score3) / acc.BF16_PEAK_TFLOPS, 4),
             "index_score_mfma_frac_of_measured": round(tf(fl_score, score3) / ceil["mfma_bf16_tflops"], 4),
+            "index_score_rate_vs_vendor_gemm_randn": round(
+                tf(fl_score, score3) / ceil["vendor_gemm_bf16_randn_tflops"], 4),
             "attn_flops": fl_attn, "score_flops": fl_score}
         # dense causal prefill baseline on the same chunk
         dfn = []
@@ -804,6 +849,7 @@ def main():
             "ms": round(dms3, 4), "flops": fl_dense,
             "mfma_frac": round(tf(fl_dense, dms3) / acc.BF16_PEAK_TFLOPS, 4),
             "mfma_frac_of_measured": round(tf(fl_dense, dms3) / ceil["mfma_bf16_tflops"], 4),
+            "rate_vs_vendor_gemm_randn": round(tf(fl_dense, dms3) / ceil["vendor_gemm_bf16_randn_tflops"], 4),
             "msa_step_speedup": round(dms3 / ms3, 2),
             "msa_sparse_attn_call_speedup": round(dms3 / attn3, 2)}}
         del dfn
