@@ -728,31 +728,36 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 // row max and sum across the four wavefronts through LDS, P (bf16) through
 // LDS, O^T = V^T P^T with each wavefront owning 32 dims.  Partial outputs and
 // log-sum-exps go where the block-major kernel puts them.
-__global__ __launch_bounds__(kDecThreads)
-void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
-                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
-                         const uint16_t* __restrict__ v_cache,
-                         const int32_t* __restrict__ block_table,
-                         const int32_t* __restrict__ seq_lens,
-                         const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
-                         int maxblk, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) DecodeShared sh;
-    if ((int)blockIdx.x >= w.small[0]) return;  // uniform
-    const int bk = w.small[1 + blockIdx.x];
-    const int cnt = w.counts[bk];
-    const int base = w.offsets[bk];
-    const int b = bk % maxblk;
-    const int g = (bk / maxblk) % Hkv;
-    const int s = bk / (maxblk * Hkv);
-    const int G = Hq / Hkv;
-    const int L = seq_lens[s];
-    const int nq = cu_q[s + 1] - cu_q[s];
-    const int pos0 = L - nq - cu_q[s];  // p = pos0 + t
-    const int nv = min(kBlock, L - b * kBlock);
-    const int page = block_table[(size_t)s * maxblk + b];
-    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
-    const uint16_t* kp = k_cache + page_off;
-    const uint16_t* vp = v_cache + page_off;
+//
+// A block is loaded (load_small: V rows, tokens at or past nv zero, then K
+// rows; tokens past nv are read from the page's padding and masked to -inf
+// later) and then attended (compute_small) against nrows rows: row rho is
+// head g G + rho % G of the (query << 4 | slot) entry entry_at(rho / G).
+// Every thread of the workgroup calls both; compute_small starts by writing
+// the V tile, so a caller that attends several blocks puts a barrier between
+// calls.
+struct SmallRaw {
+    u32x4 v[8];
+    u32x4 k[8];
+};
+
+__device__ __forceinline__ void load_small(const uint16_t* __restrict__ kp,
+                                           const uint16_t* __restrict__ vp, int nv, SmallRaw& r) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int tok = tid / 16 + 16 * it;
+        r.v[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
+    }
+    load_k_rows(kp, tid / kWave, tid % kWave, r.k);
+}
+
+template <class EntryAt>
+__device__ __forceinline__ void compute_small(DecodeShared& sh, const SmallRaw& r,
+                                              const uint16_t* __restrict__ q, int nv, int pos0,
+                                              int b, int g, int G, int Hq, int nrows,
+                                              EntryAt entry_at, const PrefillWs& w,
+                                              float scale_log2) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
@@ -760,33 +765,21 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int kg = lane / 16;  // lane group
 
     // K -> A operands of this wavefront's tokens 32w + 16j + n, dims 32i + 8kg
-    // (contiguous loads, operand order through the V tile; tokens past nv
-    // are read from the page's padding and masked to -inf later), then
-    // V -> LDS (tokens at or past nv are zero)
+    // (operand order through the V tile), then V -> LDS
     bf16x8 ka[2][4];
-    {
-        u32x4 vv[8], kraw[8];
+    k_rows_to_operands(r.k, wave, lane, sh.vs, ka);
+    __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int tok = tid / 16 + 16 * it;
-            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + 8 * (tid % 16)) : u32x4{0u, 0u, 0u, 0u};
-        }
-        load_k_rows(kp, wave, lane, kraw);
-        k_rows_to_operands(kraw, wave, lane, sh.vs, ka);
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < 8; ++it)
-            *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = vv[it];
-    }
+    for (int it = 0; it < 8; ++it)
+        *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = r.v[it];
 
-    const int nrows = cnt * G;
     for (int r0 = 0; r0 < nrows; r0 += 16) {
         // row n of this group: its query, head and slot (rows past the bucket
         // repeat its last row; their results are discarded)
         const int rho0 = r0 + n;
         const bool row_ok = rho0 < nrows;
         const int rho = row_ok ? rho0 : nrows - 1;
-        const int entry = w.entries[base + rho / G];
+        const int entry = entry_at(rho / G);
         const int t = entry >> 4;
         const int slot = entry & 15;
         const int head = g * G + rho % G;
@@ -872,6 +865,171 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     }
 }
 
+__global__ __launch_bounds__(kDecThreads)
+void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
+                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                         const uint16_t* __restrict__ v_cache,
+                         const int32_t* __restrict__ block_table,
+                         const int32_t* __restrict__ seq_lens,
+                         const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
+                         int maxblk, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    if ((int)blockIdx.x >= w.small[0]) return;  // uniform
+    const int bk = w.small[1 + blockIdx.x];
+    const int cnt = w.counts[bk];
+    const int base = w.offsets[bk];
+    const int b = bk % maxblk;
+    const int g = (bk / maxblk) % Hkv;
+    const int s = bk / (maxblk * Hkv);
+    const int G = Hq / Hkv;
+    const int L = seq_lens[s];
+    const int nq = cu_q[s + 1] - cu_q[s];
+    const int pos0 = L - nq - cu_q[s];  // p = pos0 + t
+    const int nv = min(kBlock, L - b * kBlock);
+    const int page = block_table[(size_t)s * maxblk + b];
+    const size_t page_off = ((size_t)page * Hkv + g) * kBlock * kHeadDim;
+    SmallRaw raw;
+    load_small(k_cache + page_off, v_cache + page_off, nv, raw);
+    compute_small(sh, raw, q, nv, pos0, b, g, G, Hq, cnt * G,
+                  [&](int i) { return w.entries[base + i]; }, w, scale_log2);
+}
+
+// Few queries per sequence (multi-query decode: a handful of draft tokens
+// per sequence): the inverse map's work moves into the attention kernel.
+// Workgroup (s Hkv + g, p) marks the blocks that the queries of sequence s
+// select in group g in a bitmap (in the V tile), ranks them by block index,
+// and attends each block whose rank is p modulo P once, for every entry that
+// selected it, as the block-major kernels do: one launch where the general
+// path needs the map's launches and two attention kernels.  The pages of a
+// workgroup's blocks are looked up together, in one round trip.  (Loading a
+// block's K and V during the previous block's products gains nothing: the
+// query rows each pass loads wait behind those loads.)
+constexpr int kMqEntries = 1024;                        // queries of a sequence x k, at most
+constexpr int kMqPerThread = kMqEntries / kDecThreads;  // entries held per thread
+constexpr int kMqMaxOwn = 128;                          // blocks per workgroup, at most
+constexpr int kMqMaxWords = kBlock * kHeadDim / 2;      // bitmap words the V tile holds
+
+__global__ __launch_bounds__(kDecThreads)
+void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
+                     const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
+                     const uint16_t* __restrict__ v_cache,
+                     const int32_t* __restrict__ block_table,
+                     const int32_t* __restrict__ seq_lens,
+                     const int32_t* __restrict__ cu_q,
+                     const int32_t* __restrict__ sel,       // [T, Hkv, k]
+                     PrefillWs w, int Hq, int Hkv, int maxblk, int P, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    __shared__ uint16_t rows[kMqEntries];  // entry indices of the current block's rows
+    __shared__ int own[kMqMaxOwn];         // this workgroup's blocks, in rank order
+    __shared__ int own_page[kMqMaxOwn];    // their physical pages
+    __shared__ int wtot[kDecThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int s = blockIdx.x / Hkv;
+    const int g = blockIdx.x % Hkv;
+    const int p = blockIdx.y;
+    const int G = Hq / Hkv;
+    const int t0 = cu_q[s];
+    const int nq = cu_q[s + 1] - t0;
+    const int n_e = min(nq * kTopK, kMqEntries);  // the host takes this kernel only when
+                                                  // every sequence's entries fit
+
+    // entry e = q_local k + slot of this thread: tid + 256 i; its block, or -1
+    int eb[kMqPerThread];
+#pragma unroll
+    for (int i = 0; i < kMqPerThread; ++i) {
+        const int e = tid + kDecThreads * i;
+        const int b = e < n_e ? sel[((size_t)(t0 + e / kTopK) * Hkv + g) * kTopK + e % kTopK] : -1;
+        eb[i] = (b >= 0 && b < maxblk) ? b : -1;
+    }
+    uint32_t* bits = reinterpret_cast<uint32_t*>(sh.vs);
+    const int nw = ceil_div(maxblk, 32);  // <= kMqMaxWords
+    for (int i = tid; i < nw; i += kDecThreads) bits[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMqPerThread; ++i)
+        if (eb[i] >= 0) atomicOr(&bits[eb[i] >> 5], 1u << (eb[i] & 31));
+    __syncthreads();
+
+    // a marked block's rank = the marked blocks below it: thread tid counts
+    // words [tid wpt, (tid + 1) wpt), then an exclusive prefix over threads
+    const int wpt = ceil_div(nw, kDecThreads);
+    int cnt = 0;
+    for (int k = 0; k < wpt; ++k) {
+        const int wi = tid * wpt + k;
+        if (wi < nw) cnt += __popc(bits[wi]);
+    }
+    const int incl = wave_inclusive_sum(cnt);
+    if (lane == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    int run = incl - cnt;
+    int n_marked = 0;
+#pragma unroll
+    for (int k = 0; k < kDecThreads / kWave; ++k) {
+        if (k < wave) run += wtot[k];
+        n_marked += wtot[k];
+    }
+    for (int k = 0; k < wpt; ++k) {
+        const int wi = tid * wpt + k;
+        uint32_t m = wi < nw ? bits[wi] : 0u;
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1;
+            if (run % P == p) own[run / P] = wi * 32 + bit;
+            ++run;
+        }
+    }
+    // ranks p, p + P, ... below n_marked (at most kMqMaxOwn: the host sizes P)
+    const int n_own = __builtin_amdgcn_readfirstlane(n_marked > p ? (n_marked - p + P - 1) / P : 0);
+    __syncthreads();  // own[] written; every bitmap word read (the V tile is free)
+
+    if (tid < n_own) own_page[tid] = block_table[(size_t)s * maxblk + own[tid]];
+    __syncthreads();
+
+    const int L = seq_lens[s];
+    const int pos0 = L - nq - t0;  // position of query token t: pos0 + t
+    auto nv_of = [&](int b) { return min(kBlock, L - b * kBlock); };
+    auto load_own = [&](int j, SmallRaw& r) {
+        const size_t page_off = ((size_t)own_page[j] * Hkv + g) * kBlock * kHeadDim;
+        load_small(k_cache + page_off, v_cache + page_off, nv_of(own[j]), r);
+    };
+    auto attend_own = [&](int j, const SmallRaw& r) {
+        const int b = __builtin_amdgcn_readfirstlane(own[j]);
+        // this block's rows: the entries that selected it, compacted in LDS
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < kMqPerThread; ++i) mine += (eb[i] == b);
+        const int incl_b = wave_inclusive_sum(mine);
+        __syncthreads();  // the previous block's reads of rows, wtot and the tiles are done
+        if (lane == kWave - 1) wtot[wave] = incl_b;
+        __syncthreads();
+        int at = incl_b - mine;
+        int n_rows_b = 0;
+#pragma unroll
+        for (int k = 0; k < kDecThreads / kWave; ++k) {
+            if (k < wave) at += wtot[k];
+            n_rows_b += wtot[k];
+        }
+#pragma unroll
+        for (int i = 0; i < kMqPerThread; ++i)
+            if (eb[i] == b) rows[at++] = (uint16_t)(tid + kDecThreads * i);
+        n_rows_b = __builtin_amdgcn_readfirstlane(n_rows_b);
+        __syncthreads();  // rows visible
+        compute_small(sh, r, q, nv_of(b), pos0, b, g, G, Hq, n_rows_b * G,
+                      [&](int i) {
+                          const int e = rows[i];
+                          return ((t0 + e / kTopK) << 4) | (e % kTopK);
+                      },
+                      w, scale_log2);
+    };
+    for (int j = 0; j < n_own; ++j) {
+        SmallRaw raw;
+        load_own(j, raw);
+        attend_own(j, raw);
+    }
+}
+
 // 16 threads per (query, head), 8 dims each: merge the selected slots' partials.
 __global__ __launch_bounds__(256)
 void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
@@ -948,6 +1106,26 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     const size_t map_lds = (size_t)s.maxblk * sizeof(int32_t);
     // buckets of at most small_cnt entries (kSmallRows rows) are small
     const int small_cnt = kSmallRows / (s.Hq / s.Hkv);
+    if ((int64_t)total_q * kTopK <= kMqEntries && ceil_div(s.maxblk, 32) <= kMqMaxWords) {
+        // a few queries per sequence: one kernel finds each (sequence, group)'s
+        // blocks and attends them.  P workgroups per (sequence, group): about
+        // eight blocks each when the queries are spread evenly over the
+        // sequences, and never more than kMqMaxOwn.  Each workgroup repeats
+        // the union, so fewer and longer ones win up to a point: at 8 x 60k
+        // with 4 drafts the attention call took 66.5, 58.5, 54.0 and 52.5 us
+        // at 1, 2, 4 and 8 blocks per workgroup with the pages looked up per
+        // block, and 48.6 and 59.8 us at 8 and 16 with the lookups together.
+        const int u_avg = std::min(s.maxblk, ceil_div(total_q, s.B) * kTopK);
+        const int u_max = std::min(s.maxblk, total_q * kTopK);
+        const int P = std::max({1, ceil_div(u_avg, 8), ceil_div(u_max, kMqMaxOwn)});
+        hipLaunchKernelGGL(mq_block_kernel, dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0, st, q,
+                           k_cache, v_cache, block_table, seq_lens, cu_q, sel, w, s.Hq, s.Hkv,
+                           s.maxblk, P, s.scale * kLog2e);
+        const int nth = total_q * s.Hq * 16;
+        hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel,
+                           w, out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
+        return hipGetLastError();
+    }
     if (NB <= kSmallMapBuckets && (int64_t)total_q * s.Hkv * kTopK <= kSmallMapSel) {
         hipLaunchKernelGGL(inverse_map_small_kernel, dim3(1), dim3(kSmallMapThreads), 0, st, sel, cu_q, w,
                            total_q, s.B, s.Hkv, s.maxblk, small_cnt);

@@ -23,6 +23,14 @@ KV groups), how many page slots one workgroup attends: one while all 16 R
 page workgroups fit on the chip at once (R <= 64), else 2, 4 or 8
 (decode_multi_kernel<NPT, W, PAGES, slots>: R < 128, R < 256, R >= 256).
 MULTI covers each of those with short and long rows.
+
+msa_sparse_attn_prefill picks its form by the number of queries T and the
+row width: with T x k <= 1024 (a few draft tokens per sequence)
+mq_block_kernel finds each (sequence, group)'s union of selected blocks itself
+and attends each block once for all the drafts that chose it; otherwise an
+inverse map (one workgroup while the buckets and selections are few, else
+four kernels) feeds the block-major kernel (buckets of more than 32 rows) and
+the small-bucket kernel.  MQ covers the first form's limits and the switch.
 """
 import numpy as np
 import pytest
@@ -140,3 +148,28 @@ def test_multi_page_workgroups(cfg):
     assert torch.equal(fused.sel, step.sel)
     assert torch.equal(fused.out, step.out)
     assert torch.equal(fused.lse, step.lse)
+
+
+MQ = [
+    # 60 of the 64 queries in one sequence (its union spans many workgroups
+    # of about eight blocks), a sequence with none
+    gen.MsaConfig("mq_skewed_64", [30_000, 9_000, 5_000, 700], [60, 0, 3, 1], 48, 8,
+                  permute_pages=True, seed=101),
+    # exactly 64 queries in one sequence: every entry slot of the kernel used
+    gen.MsaConfig("mq_one_seq_64", [16_000], [64], 16, 2, permute_pages=True, seed=102),
+    # 65 queries: past the kernel's limit, the one-workgroup inverse map
+    gen.MsaConfig("mq_one_seq_65", [16_000], [65], 16, 2, permute_pages=True, seed=103),
+    # G = 1, drafts of several lengths
+    gen.MsaConfig("mq_g1", [5_000, 12_000, 800], [4, 7, 2], 4, 4, permute_pages=True, seed=104),
+    # a 2,097,152-token row (16,384 blocks: two bitmap words per thread)
+    gen.MsaConfig("mq_2m_tokens", [16384 * 128, 3_000], [3, 2], 8, 1, permute_pages=True,
+                  seed=105),
+]
+
+
+@pytest.mark.parametrize("cfg", MQ, ids=lambda c: c.name)
+def test_multi_query_kernel(cfg):
+    """Few queries per sequence through msa_sparse_attn_prefill: scores,
+    selection and every attention row against the oracle, padding poisoned."""
+    print(f"[mq] {cfg.name} T={cfg.total_q} maxblk={cfg.max_blocks}", flush=True)
+    parity.full_check(cfg, poison=True, attn_rows=cfg.total_q * cfg.num_q_heads)

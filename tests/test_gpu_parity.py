@@ -794,17 +794,18 @@ def test_dense_prefill_equals_msa_when_every_block_is_selected():
 
 
 @pytest.mark.parametrize("cfg", [
-    # G = 6: buckets of up to 5 queries (30 rows, two 16-row groups) take the
-    # small-bucket kernel; the drafts' shared own block holds 5 or 6 queries
+    # G = 6: a block chosen by up to 5 drafts is 30 rows (two 16-row
+    # passes); the drafts' shared own block holds 5 or 6 queries (36 rows)
     gen.MsaConfig("mq_g6_5drafts", [9000, 20000, 4100], [5, 6, 5], 48, 8, permute_pages=True,
                   seed=54),
     # G = 16: at most 2 queries (32 rows) per small bucket
     gen.MsaConfig("mq_g16_3drafts", [7000, 3000], [3, 2], 16, 1, permute_pages=True, seed=55),
 ], ids=lambda c: c.name)
 def test_small_and_large_buckets(cfg):
-    """Few queries per sequence split the (sequence, group, block) buckets
-    between the small-bucket kernel and the block-major kernel; every output
-    row against the oracle."""
+    """Few queries per sequence (the multi-query kernel: each (sequence,
+    group)'s union of selected blocks, each block attended once for all the
+    drafts that chose it, in 16-row passes); every output row against the
+    oracle."""
     print(f"[buckets] {cfg.name}", flush=True)
     parity.full_check(cfg, poison=True)
 
