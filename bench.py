@@ -58,7 +58,10 @@ def parse():
     ap.add_argument("--score-only", action="store_true",
                     help="only run the headline's index_score_kernel calls (PMC passes)")
     ap.add_argument("--step-only", action="store_true",
-                    help="only run the headline's msa_decode_step layer-steps (PMC passes)")
+                    help="only run msa_decode_step layer-steps of --config (PMC passes)")
+    ap.add_argument("--config", type=int, default=2, choices=(2, 4, 5),
+                    help="decode workload of --step-only: 2 = 8 x 60k (headline), 4 = 4 x 1M, "
+                         "5 = ragged 16 sequences")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run chunked-prefill layer-steps, 8192 tokens on 57,344 (PMC passes)")
     ap.add_argument("--gemm-probe", action="store_true",
@@ -68,7 +71,8 @@ def parse():
     ap.add_argument("--record-traffic", nargs=5,
                     metavar=("RECORD", "COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                     help="write traffic record RECORD (index_score: --score-only passes; "
-                         "decode_step: --step-only passes) from four rocprofv3 --pmc counter "
+                         "decode_step, decode_step_1m, decode_step_ragged: --step-only "
+                         "--config 2, 4, 5 passes) from four rocprofv3 --pmc counter "
                          "CSVs (copy calibration FETCH_SIZE, WRITE_SIZE; the workload's "
                          "FETCH_SIZE, WRITE_SIZE) and exit; needs no GPU")
     return ap.parse_args()
@@ -372,18 +376,37 @@ def cpu_baseline(cfg, x, budget_s):
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, keyed by the SHA-256 of the
 # sources the kernels are built from, so that a later change voids them.
 CSRC = "block_sparse_attention_03_amd/csrc"
+_STEP_SOURCES = ["index_score.hip", "decode_attn.hip", "select.hpp", "decode_tile.hpp",
+                 "msa_common.hpp"]
 TRAFFIC = {
     "index_score": {
         "file": "profiles/index_score_decode_60k_traffic.json",
+        "config": 2,
         "sources": ["index_score.hip"],
         "kernels": ["index_score_kernel<true, false>"],
         "what": "index_score_kernel (the msa_index_score form) per launch",
     },
     "decode_step": {
         "file": "profiles/decode_step_60k_traffic.json",
-        "sources": ["index_score.hip", "decode_attn.hip", "select.hpp", "decode_tile.hpp",
-                    "msa_common.hpp"],
+        "config": 2,
+        "sources": _STEP_SOURCES,
         "kernels": ["index_score_kernel<false, false>", "decode_fused_kernel<8, 1, true>",
+                    "decode_merge_kernel"],
+        "what": "msa_decode_step's three kernels, summed per layer-step",
+    },
+    "decode_step_1m": {
+        "file": "profiles/decode_step_1m_traffic.json",
+        "config": 4,
+        "sources": _STEP_SOURCES,
+        "kernels": ["index_score_kernel<false, false>", "decode_fused_kernel<32, 4, false>",
+                    "decode_merge_kernel"],
+        "what": "msa_decode_step's three kernels, summed per layer-step",
+    },
+    "decode_step_ragged": {
+        "file": "profiles/decode_step_ragged_traffic.json",
+        "config": 5,
+        "sources": _STEP_SOURCES,
+        "kernels": ["index_score_kernel<false, false>", "decode_multi_kernel<16, 4, true, 4>",
                     "decode_merge_kernel"],
         "what": "msa_decode_step's three kernels, summed per layer-step",
     },
@@ -452,12 +475,14 @@ def traffic_record(name, copy_f, copy_w, fetch, write, srcs):
                         "write_size_kib_per_launch": round(kw, 1),
                         "fetch_bytes_per_launch": int(round(kf * 1024 * ff)),
                         "write_bytes_per_launch": int(round(kw * 1024 * fw))})
-    cfg = gen.config(2)
-    algo = acc.score_bytes(cfg) + (acc.decode_attn_bytes(cfg) if name == "decode_step" else 0)
+    cfg = gen.config(spec["config"])
+    algo = acc.score_bytes(cfg) + (acc.decode_attn_bytes(cfg) if name.startswith("decode_step") else 0)
+    lens = (f"{cfg.seq_lens[0]:,} tokens" if len(set(cfg.seq_lens)) == 1
+            else f"{min(cfg.seq_lens):,} to {max(cfg.seq_lens):,} tokens")
     return {
         "record": name,
         "what": spec["what"],
-        "workload": f"paged decode, {cfg.num_seqs} sequences x {cfg.seq_lens[0]:,} tokens, "
+        "workload": f"paged decode ({cfg.name}), {cfg.num_seqs} sequences x {lens}, "
                     f"H_kv {cfg.num_kv_heads}, H_idx {cfg.num_idx_heads}",
         "source_sha256": sources_sha256(srcs),
         "sources": [f"{CSRC}/{f}" for f in spec["sources"]],
@@ -658,8 +683,9 @@ def main():
         print(json.dumps({"index_score_ms": ms, "launches": args.steps + args.warmup}))
         return
     if args.step_only:
-        cfg = gen.config(2)
-        fused = [MsaStep(x, fused=True) for x in make_layers(cfg, args.layers)]
+        cfg = gen.config(args.config)
+        n_layers = args.layers if args.config == 2 else 2  # 18 GB per 1M layer
+        fused = [MsaStep(x, fused=True) for x in make_layers(cfg, n_layers)]
         ms = time_calls([s_.run for s_ in fused], args.steps, args.warmup)
         print(json.dumps({"decode_step_ms": ms, "layer_steps": args.steps + args.warmup}))
         return
@@ -744,7 +770,7 @@ def main():
         cpu_cfg = {}  # the oracle's stages per workload (CPU baseline)
         want_cpu = not args.no_cpu_baseline
 
-        def decode_line(c, n_layers, n_steps, graph=False, cpu=False):
+        def decode_line(c, n_layers, n_steps, graph=False, cpu=False, record=None):
             ls = make_layers(c, n_layers)
             if cpu and want_cpu:
                 cpu_cfg[c.name] = cpu_stages(c, ls[0])
@@ -759,6 +785,8 @@ def main():
                     "us_four_calls": round(ms4_ * 1e3, 2), "layers": n_layers}
             if graph:  # launch-bound: the same steps replayed as one HIP graph per pass
                 line["us_hip_graph"] = round(time_graph(f, 4 * n_layers, 2 * n_layers) * 1e3, 2)
+            if record:  # HBM bytes per layer-step counted by rocprofv3 (null if stale)
+                line["traffic"] = recorded_traffic(record)
             del f, fo, ls
             torch.cuda.empty_cache()
             return line
@@ -771,7 +799,8 @@ def main():
         also["paged_decode_b8_ctx60k_per_group_index_keys"] = decode_line(cg, 4, max(40, args.steps // 4))
         # ragged decode: 16 sequences, 4096 .. 524,288 tokens, 128 flattened rows
         c5 = gen.config(5)
-        also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4), cpu=True)
+        also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4), cpu=True,
+                                    record="decode_step_ragged")
         # multi-query decode: 4 draft tokens per sequence on the 60k workload,
         # through msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill
         import dataclasses
@@ -799,6 +828,8 @@ def main():
         dense[c4.name] = dense_line(c4, l4, 6, ms4)
         also[c4.name] = {"us_per_layer_step": round(ms4 * 1e3, 2),
                          "layer_step_hbm_frac": round(b4 / (ms4 * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": int(b4),
+                         "traffic": recorded_traffic("decode_step_1m"),
                          "us_four_calls": round(time_calls([s.run for s in s4], n4, 2) * 1e3, 2),
                          "scoring_pass": roofline_entry("index_score_kernel", acc.score_bytes(c4), score4)}
         del f4, s4, l4

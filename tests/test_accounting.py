@@ -1,6 +1,7 @@
 """The algorithmic-work accounting behind bench.py's roofline numbers."""
 import json
 import os
+import pytest
 
 from block_sparse_attention_03_amd import accounting as acc
 from block_sparse_attention_03_amd import inputs as gen
@@ -108,4 +109,35 @@ def test_decode_step_traffic_record_sums_its_three_kernels(tmp_path):
     assert rec["write_bytes_per_launch"] == int((1 + 3 + 0.5) * 1024)
     assert rec["source_sha256"] == hashlib.sha256(b"part 0part 1").hexdigest()
     cfg = gen.config(2)
+    assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
+
+
+@pytest.mark.parametrize("name,cfg_i,paged", [("decode_step_1m", 4, "decode_fused_kernel<32, 4, false>"),
+                                              ("decode_step_ragged", 5,
+                                               "decode_multi_kernel<16, 4, true, 4>")])
+def test_step_records_of_the_1m_and_ragged_decode(tmp_path, name, cfg_i, paged):
+    """The 1M and ragged decode-step records take the page kernel form those
+    workloads run (and no other page kernel), and the workload's own
+    algorithmic bytes."""
+    import bench
+    ns = "void msa::(anonymous namespace)::"
+    score = ns + "index_score_kernel<false, false>(unsigned short const*)"
+    page = ns + paged + "(float const*)"
+    other = ns + "decode_fused_kernel<8, 1, true>(float const*)"
+    merge = ns + "decode_merge_kernel(int const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    p = {k: str(tmp_path / f"{k}.csv") for k in ("cf", "cw", "f", "w")}
+    _counter_csv(p["cf"], [(copy, "FETCH_SIZE", 131072.0)])
+    _counter_csv(p["cw"], [(copy, "WRITE_SIZE", 262144.0)])
+    _counter_csv(p["f"], [(score, "FETCH_SIZE", 10.0), (page, "FETCH_SIZE", 20.0),
+                          (other, "FETCH_SIZE", 999.0), (merge, "FETCH_SIZE", 1.0)])
+    _counter_csv(p["w"], [(score, "WRITE_SIZE", 1.0), (page, "WRITE_SIZE", 2.0),
+                          (other, "WRITE_SIZE", 999.0), (merge, "WRITE_SIZE", 1.0)])
+    src = tmp_path / "s.hip"
+    src.write_bytes(b"x")
+    rec = bench.traffic_record(name, p["cf"], p["cw"], p["f"], p["w"], [str(src)])
+    assert [k["kernel"] for k in rec["kernels"]] == ["index_score_kernel<false, false>", paged,
+                                                     "decode_merge_kernel"]
+    assert rec["fetch_bytes_per_launch"] == (10 + 20 + 1) * 1024 * 2
+    cfg = gen.config(cfg_i)
     assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
