@@ -141,6 +141,48 @@ def time_calls(fns, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def step_percentiles(fns, steps, warmup):
+    """p10 / p50 / p90 of single-call times (µs), cycling over fns: an event
+    before each call and one after the last, all on the stream the calls run
+    on, back to back (no synchronisation between calls)."""
+    import torch
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    evs = [HipEvent() for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record()
+        fns[i % len(fns)]()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
+    pick = lambda q: round(t[min(steps - 1, int(q * steps))], 2)  # noqa: E731
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "calls": steps}
+
+
+def parse_max_clock_mhz(rocminfo_text):
+    """Max Clock Freq. (MHz) of the first gfx950 agent in rocminfo's output,
+    or None."""
+    for agent in rocminfo_text.split("*******"):
+        if "gfx950" not in agent or "Max Clock Freq. (MHz):" not in agent:
+            continue
+        try:
+            return int(agent.split("Max Clock Freq. (MHz):")[1].split()[0])
+        except (IndexError, ValueError):
+            return None
+    return None
+
+
+def gpu_max_clock_mhz():
+    """The GPU agent's maximum engine clock as rocminfo reports it, or None."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return parse_max_clock_mhz(txt)
+
+
 def dense_calls(xs):
     """msa_dense_attn_decode (the dense GQA baseline) on each layer's inputs,
     with its buffers allocated once."""
@@ -581,6 +623,7 @@ def measured_ceilings():
     del buf
     torch.cuda.empty_cache()
     vendor = vendor_gemm_tflops()
+    clock = gpu_max_clock_mhz()
     gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
     gc = max(copy, key=copy.get)
     gcs = max(copy_small, key=copy_small.get)
@@ -591,6 +634,7 @@ def measured_ceilings():
             "mfma_bf16_tflops": round(tflops[bm], 1),
             "vendor_gemm_bf16_randn_tflops": round(vendor["randn"], 1),
             "vendor_gemm_bf16_const_tflops": round(vendor["const"], 1),
+            "gpu_max_clock_mhz": clock,
             "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
                    f"and of 64 MiB slices back to back (best grid {gs}); a device copy of 800 MiB "
                    f"(read + write bytes, best grid {gc}) and of 96 MiB (best grid {gcs}); 32x32x16 bf16 MFMA "
@@ -698,6 +742,7 @@ def main():
     fused_ms = time_calls([s.run for s in fused], args.steps, args.warmup)
     four_ms = time_calls([s.run for s in four], args.steps, args.warmup)
     graph_ms = time_graph(fused, args.steps, args.warmup)
+    per_step = step_percentiles([s.run for s in fused], args.steps, args.warmup)
     # the scoring pass alone (msa_index_score: the same index_score_kernel)
     score_ms = time_calls([s.score for s in four], args.steps, args.warmup)
     attn_ms = time_calls([s.attend for s in four], args.steps, args.warmup)
@@ -739,6 +784,8 @@ def main():
                        "scoring_pass": roofline_entry("index_score_kernel", acc.score_bytes(cfg),
                                                       score_ms, recorded_traffic("index_score")),
                        "select_attend_merge_us": round((fused_ms - score_ms) * 1e3, 2),
+                       # each layer-step timed on its own (an event pair per call)
+                       "per_step_us": per_step,
                        "us_hip_graph": round(graph_ms * 1e3, 2),
                        "us_four_calls": round(four_ms * 1e3, 2),
                        "hbm_frac_four_calls": frac(four_ms),

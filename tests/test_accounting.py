@@ -141,3 +141,13 @@ def test_step_records_of_the_1m_and_ragged_decode(tmp_path, name, cfg_i, paged):
     assert rec["fetch_bytes_per_launch"] == (10 + 20 + 1) * 1024 * 2
     cfg = gen.config(cfg_i)
     assert rec["algorithmic_bytes_per_launch"] == acc.score_bytes(cfg) + acc.decode_attn_bytes(cfg)
+
+
+def test_rocminfo_clock_parse_takes_the_gfx950_agent():
+    """The bench's clock field comes from the GPU agent's block of rocminfo's
+    output, not the CPU agent's."""
+    import bench
+    txt = ("*******\nAgent 1\n*******\n  Name: AMD EPYC\n  Max Clock Freq. (MHz):   3700\n"
+           "*******\nAgent 2\n*******\n  Name: gfx950\n  Max Clock Freq. (MHz):   2400\n")
+    assert bench.parse_max_clock_mhz(txt) == 2400
+    assert bench.parse_max_clock_mhz("Name: gfx942\n  Max Clock Freq. (MHz): 2100\n") is None
