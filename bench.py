@@ -856,8 +856,15 @@ def main():
         lm = make_layers(cm, 4)
         sm = [MsaStep(x) for x in lm]
         msm = time_calls([st.run for st in sm], max(20, args.steps // 4), 4)
+        # bytes: index keys once for all drafts, each (sequence, group)'s union
+        # of selected blocks once (from each layer's own selection), rows and
+        # partials per selection; averaged over the layers
+        bm = sum(acc.score_bytes(cm) + acc.multi_query_attn_bytes(cm, st.sel.cpu().numpy())
+                 for st in sm) / len(sm)
         also[cm.name] = {"us_per_layer_step": round(msm * 1e3, 2),
                          "us_per_query_token": round(msm * 1e3 / cm.total_q, 2),
+                         "algorithmic_bytes": int(bm),
+                         "layer_step_hbm_frac": round(bm / (msm * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
                          "layers": 4}
         del sm, lm
         torch.cuda.empty_cache()

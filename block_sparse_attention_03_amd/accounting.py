@@ -82,6 +82,34 @@ def prefill_attn_bytes(cfg) -> int:
     return kv + q + partial + out
 
 
+def multi_query_attn_bytes(cfg, sel) -> int:
+    """Few queries per sequence, block-major over each (sequence, group)'s
+    union of selected blocks (sel: [total_q, H_kv, k] block indices, -1 for
+    none, the call's own selection): K and V of every block in a union once
+    (its tokens up to the sequence end), q read once per (query, head, slot),
+    the partial outputs (bf16) and LSEs (fp32) written and read back once,
+    out + lse written."""
+    D, Bk = cfg.head_dim, cfg.block_size
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    kv_tokens = 0
+    slots = 0
+    t = 0
+    for L, n in zip(cfg.seq_lens, cfg.n_new):
+        for g in range(cfg.num_kv_heads):
+            union = set()
+            for i in range(n):
+                row = [int(b) for b in sel[t + i][g] if b >= 0]
+                union.update(row)
+                slots += len(row)
+            kv_tokens += sum(min(Bk, L - b * Bk) for b in union)
+        t += n
+    kv = kv_tokens * 2 * D * 2
+    q = slots * G * D * 2
+    partial = slots * G * (D * 2 + 4) * 2
+    out = cfg.total_q * cfg.num_q_heads * (D * 2 + 4)
+    return kv + q + partial + out
+
+
 def dense_over_msa_flops(L: int, num_q_heads: int, num_idx_q_heads: int, head_dim: int = 128,
                          idx_dim: int = 64, budget: int = 2048) -> float:
     """Attention flops per token of dense GQA over those of MSA at context L.

@@ -1,6 +1,7 @@
 """The algorithmic-work accounting behind bench.py's roofline numbers."""
 import json
 import os
+import numpy as np
 import pytest
 
 from block_sparse_attention_03_amd import accounting as acc
@@ -151,3 +152,21 @@ def test_rocminfo_clock_parse_takes_the_gfx950_agent():
            "*******\nAgent 2\n*******\n  Name: gfx950\n  Max Clock Freq. (MHz):   2400\n")
     assert bench.parse_max_clock_mhz(txt) == 2400
     assert bench.parse_max_clock_mhz("Name: gfx942\n  Max Clock Freq. (MHz): 2100\n") is None
+
+
+def test_multi_query_bytes_count_each_union_block_once():
+    """Two drafts of one sequence that share their own block and one other:
+    the union's blocks are read once each, the rows once per selection."""
+    cfg = gen.MsaConfig("mq_bytes", [300], [2], 4, 2)
+    sel = np.full((2, 2, cfg.topk), -1, np.int32)
+    sel[0, 0, :2] = [0, 2]
+    sel[1, 0, :3] = [0, 1, 2]
+    sel[0, 1, :1] = [2]
+    sel[1, 1, :2] = [1, 2]
+    D, G = 128, 2
+    # group 0: union {0, 1, 2}; group 1: union {1, 2}; block 2 holds 300 - 256 = 44 tokens
+    kv_tokens = (128 + 128 + 44) + (128 + 44)
+    slots = 2 + 3 + 1 + 2
+    want = (kv_tokens * 2 * D * 2 + slots * G * D * 2 + slots * G * (2 * D + 4) * 2
+            + 2 * 4 * (2 * D + 4))
+    assert acc.multi_query_attn_bytes(cfg, sel) == want
