@@ -199,6 +199,24 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ q,
     compute_page(qb, pr, nv, G, r, slot, ws, R, scale_log2, sh);
 }
 
+// The (row, workgroup-within-row) of a page workgroup on an (n_x, R) grid.
+// Workgroups reach the 8 XCDs round-robin by linear id; when R is a
+// multiple of 8 the k-th workgroup on XCD x takes row (k / n_x) * 8 + x, so
+// that all n_x workgroups of a row share one L2 and what they all read of
+// the row (its scores and block-table entries, or its page-table row, and
+// its queries) comes from memory once (same-box A/Bs: 4 x 1M decode
+// 0.3-1% faster, ragged 16-sequence decode 0.6%, 8 x 60k within noise).
+__device__ __forceinline__ void xcd_row(int n_x, int R, int* x, int* r) {
+    if (R % 8 != 0) {
+        *x = blockIdx.x;
+        *r = blockIdx.y;
+        return;
+    }
+    const int lin = blockIdx.y * n_x + blockIdx.x;
+    *x = (lin / 8) % n_x;
+    *r = (lin / 8 / n_x) * 8 + lin % 8;
+}
+
 __global__ __launch_bounds__(kDecThreads)
 void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
@@ -207,8 +225,8 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
                         const int32_t* __restrict__ row_lens,    // [R]
                         void* __restrict__ ws, int Hq, int Hkv, int R, float scale_log2) {
     __shared__ __attribute__((aligned(16))) DecodeShared sh;
-    const int slot = blockIdx.x;
-    const int r = blockIdx.y;
+    int slot, r;
+    xcd_row(kTopK, R, &slot, &r);
     const int n_tok = row_lens[r];
     if (slot * kBlock >= n_tok) return;  // page not used by this row (uniform)
     const int nv = min(kBlock, n_tok - slot * kBlock);
@@ -228,23 +246,6 @@ void decode_page_kernel(const uint16_t* __restrict__ q,        // [B, Hq, 128]
 // chip -- and attends that page.  Slot 0 also publishes the row's selection
 // and length.  With PAGES the block-table entries are loaded beside the
 // scores, so the selection hands over pages directly.
-// The (row, workgroup-within-row) of a page workgroup on an (n_x, R) grid.
-// Workgroups reach the 8 XCDs round-robin by linear id; when R is a
-// multiple of 8 the k-th workgroup on XCD x takes row (k / n_x) * 8 + x, so
-// that all n_x workgroups of a row share one L2 and the row's scores and
-// block-table entries come from memory once (same-box A/Bs: 4 x 1M decode
-// 0.3-1% faster, ragged 16-sequence decode 0.6%, 8 x 60k within noise).
-__device__ __forceinline__ void xcd_row(int n_x, int R, int* x, int* r) {
-    if (R % 8 != 0) {
-        *x = blockIdx.x;
-        *r = blockIdx.y;
-        return;
-    }
-    const int lin = blockIdx.y * n_x + blockIdx.x;
-    *x = (lin / 8) % n_x;
-    *r = (lin / 8 / n_x) * 8 + lin % 8;
-}
-
 template <int NPT, int W, bool PAGES>
 __global__ __launch_bounds__(kDecThreads)
 void decode_fused_kernel(const float* __restrict__ scores,     // [B, Hkv, maxblk]
