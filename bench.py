@@ -848,26 +848,32 @@ def main():
         c5 = gen.config(5)
         also[c5.name] = decode_line(c5, 2, max(20, args.steps // 4), cpu=True,
                                     record="decode_step_ragged")
-        # multi-query decode: 4 draft tokens per sequence on the 60k workload,
-        # through msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill
+        # multi-query decode: 4 and 8 draft tokens per sequence on the 60k
+        # workload, as msa_multi_query_step and as its three calls
+        # (msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill)
         import dataclasses
-        cm = dataclasses.replace(gen.config(2), name="multi_query_decode_b8_ctx60k_4drafts",
-                                 n_new=[4] * 8)
-        lm = make_layers(cm, 4)
-        sm = [MsaStep(x) for x in lm]
-        msm = time_calls([st.run for st in sm], max(20, args.steps // 4), 4)
-        # bytes: index keys once for all drafts, each (sequence, group)'s union
-        # of selected blocks once (from each layer's own selection), rows and
-        # partials per selection; averaged over the layers
-        bm = sum(acc.score_bytes(cm) + acc.multi_query_attn_bytes(cm, st.sel.cpu().numpy())
-                 for st in sm) / len(sm)
-        also[cm.name] = {"us_per_layer_step": round(msm * 1e3, 2),
-                         "us_per_query_token": round(msm * 1e3 / cm.total_q, 2),
-                         "algorithmic_bytes": int(bm),
-                         "layer_step_hbm_frac": round(bm / (msm * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
-                         "layers": 4}
-        del sm, lm
-        torch.cuda.empty_cache()
+        for nd in (4, 8):
+            cm = dataclasses.replace(gen.config(2), name=f"multi_query_decode_b8_ctx60k_{nd}drafts",
+                                     n_new=[nd] * 8)
+            lm = make_layers(cm, 4)
+            sm = [MsaStep(x, multi=True) for x in lm]
+            s3 = [MsaStep(x) for x in lm]
+            n_m = max(20, args.steps // 4)
+            msm = time_calls([st.run for st in sm], n_m, 4)
+            ms3 = time_calls([st.run for st in s3], n_m, 4)
+            # bytes: index keys once for all drafts, each (sequence, group)'s
+            # union of selected blocks once (from each layer's own selection),
+            # rows and partials per selection; averaged over the layers
+            bm = sum(acc.score_bytes(cm) + acc.multi_query_attn_bytes(cm, st.sel.cpu().numpy())
+                     for st in sm) / len(sm)
+            also[cm.name] = {"us_per_layer_step": round(msm * 1e3, 2),
+                             "us_per_query_token": round(msm * 1e3 / cm.total_q, 2),
+                             "us_three_calls": round(ms3 * 1e3, 2),
+                             "algorithmic_bytes": int(bm),
+                             "layer_step_hbm_frac": round(bm / (msm * 1e-3) / 1e9 / acc.HBM_PEAK_GBS, 4),
+                             "entry_point": "msa_multi_query_step", "layers": 4}
+            del sm, s3, lm
+            torch.cuda.empty_cache()
         # 1M-context decode, batch 4 (18 GB of K/V per layer): 2 layers
         c4 = gen.config(4)
         l4 = make_layers(c4, 2)

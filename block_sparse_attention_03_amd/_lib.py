@@ -30,6 +30,7 @@ EXPORTED = (
     "msa_status_string", "msa_abi_version", "msa_decode_step", "msa_decode_step_workspace_size",
     "msa_dense_attn_decode", "msa_dense_decode_workspace_size", "msa_dense_attn_prefill",
     "msa_validate_inputs", "msa_append_kv", "msa_decode_step_append", "msa_decode_step_noalloc",
+    "msa_multi_query_step", "msa_multi_query_step_workspace_size",
 )
 
 MSA_STATIC_SCRATCH_BYTES = 32 << 20  # include/msa.h
@@ -80,6 +81,9 @@ def lib():
         L.msa_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
         L.msa_decode_step_workspace_size.argtypes = [D]
         L.msa_decode_step_workspace_size.restype = SZ
+        L.msa_multi_query_step.argtypes = [D, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.msa_multi_query_step_workspace_size.argtypes = [D, I32]
+        L.msa_multi_query_step_workspace_size.restype = SZ
         L.msa_dense_attn_decode.argtypes = [D, P, P, P, P, P, P, P, P, SZ, P]
         L.msa_dense_attn_prefill.argtypes = [D, I32, P, P, P, P, P, P, P, P, P]
         L.msa_validate_inputs.argtypes = [D, I32, P, P, P, P, P]
@@ -89,7 +93,8 @@ def lib():
         for f in ("msa_index_score", "msa_topk_blocks", "msa_build_page_table",
                   "msa_sparse_attn_decode", "msa_sparse_attn_prefill", "msa_decode_step",
                   "msa_dense_attn_decode", "msa_dense_attn_prefill", "msa_validate_inputs",
-                  "msa_append_kv", "msa_decode_step_append", "msa_decode_step_noalloc"):
+                  "msa_append_kv", "msa_decode_step_append", "msa_decode_step_noalloc",
+                  "msa_multi_query_step"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_decode_workspace_size.argtypes = [D]
         L.msa_decode_workspace_size.restype = SZ
@@ -317,6 +322,40 @@ def msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, s
                     sel, workspace, stream=None):
     prepare_msa_decode_step(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens,
                             out, lse, sel, workspace)(stream)
+
+
+def msa_multi_query_step_workspace_size(dims, total_q: int) -> int:
+    return int(lib().msa_multi_query_step_workspace_size(ctypes.byref(dims), total_q))
+
+
+def prepare_msa_multi_query_step(dims, total_q, q_idx, kidx_cache, q, k_cache, v_cache,
+                                 block_table, seq_lens, cu_q, out, lse, sel, workspace):
+    """msa_multi_query_step with its arguments checked and packed once: returns
+    a PreparedCall that repeats the call, on the current (or a given) stream."""
+    d = dims
+    B, Hq, H, T = d.num_seqs, d.num_q_heads, d.num_kv_heads, total_q
+    cache = (d.num_pages, H, d.block_size, d.head_dim)
+    args = (_ptr(q_idx, BF16, "q_idx", (T, H, d.idx_dim)),
+            _ptr(kidx_cache, BF16, "kidx_cache", (d.num_pages, d.num_idx_heads, d.block_size, d.idx_dim)),
+            _ptr(q, BF16, "q", (T, Hq, d.head_dim)), _ptr(k_cache, BF16, "k_cache", cache),
+            _ptr(v_cache, BF16, "v_cache", cache),
+            _ptr(block_table, I32, "block_table", (B, d.max_blocks_per_seq)),
+            _ptr(seq_lens, I32, "seq_lens", (B,)), _ptr(cu_q, I32, "cu_q", (B + 1,)),
+            _ptr(out, BF16, "out", (T, Hq, d.head_dim)),
+            _ptr(lse, F32, "lse", (T, Hq)) if lse is not None else None,
+            _ptr(sel, I32, "sel", (T, H, d.topk)) if sel is not None else None,
+            _ptr(workspace, torch.uint8, "workspace"))
+    nbytes = workspace.numel() if workspace is not None else 0
+    return PreparedCall(lib().msa_multi_query_step, (ctypes.byref(d), T, *args, nbytes),
+                        "msa_multi_query_step",
+                        (d, q_idx, kidx_cache, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                         out, lse, sel, workspace))
+
+
+def msa_multi_query_step(dims, total_q, q_idx, kidx_cache, q, k_cache, v_cache, block_table,
+                         seq_lens, cu_q, out, lse, sel, workspace, stream=None):
+    prepare_msa_multi_query_step(dims, total_q, q_idx, kidx_cache, q, k_cache, v_cache,
+                                 block_table, seq_lens, cu_q, out, lse, sel, workspace)(stream)
 
 
 def prepare_msa_decode_step_noalloc(dims, q_idx, kidx_cache, q, k_cache, v_cache, block_table,

@@ -475,7 +475,13 @@ hipError_t msa_launch_index_score(const MsaShape& s, int total_q, const uint16_t
     using namespace msa;
     if (total_q == 0) return hipSuccess;
     const int R = (s.Hidx == 1) ? s.Hkv : 1;
-    if (total_q > 4 * s.B) {
+    // Up to 128 queries per sequence on average the per-block kernel (each
+    // block's keys loaded once for all of its sequence's rows) is faster:
+    // scoring 8 x 60k with 8, 32, 128 or 256 queries per sequence took 16.6,
+    // 38.0, 111.5 and 197 us there against 150, 151, 160 and 164 us in the
+    // GEMM form, whose few 1,024-row groups leave most of the chip idle at
+    // these sizes.
+    if (total_q > 128 * s.B) {
         // many queries per sequence on average: GEMM form.  Upper bound on the
         // number of row groups: sum_s ceil(nq_s R / rows) <= total_q R / rows + B.
         const int groups = ceil_div(total_q * R, kGRows) + s.B;

@@ -168,6 +168,40 @@ msa_status_t msa_sparse_attn_prefill(const msa_dims_t* dims, int32_t total_q, co
                                        sel, out, lse, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t msa_multi_query_step_workspace_size(const msa_dims_t* dims, int32_t total_q) {
+    MsaShape s;
+    if (check_dims(dims, &s) != MSA_SUCCESS || check_total_q(s, total_q) != MSA_SUCCESS) return 0;
+    return msa_multi_query_ws_bytes(s, total_q);
+}
+
+msa_status_t msa_multi_query_step(const msa_dims_t* dims, int32_t total_q, const uint16_t* q_idx,
+                                  const uint16_t* kidx_cache, const uint16_t* q,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens,
+                                  const int32_t* cu_q, uint16_t* out, float* lse, int32_t* sel,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    MsaShape s;
+    msa_status_t st = check_dims(dims, &s);
+    if (st != MSA_SUCCESS) return st;
+    if ((st = check_total_q(s, total_q)) != MSA_SUCCESS) return st;
+    if (total_q == 0) return MSA_SUCCESS;  // no work: nothing read, nothing launched
+    if (!q_idx || !kidx_cache || !q || !k_cache || !v_cache || !block_table || !seq_lens ||
+        !cu_q || !out)
+        return MSA_ERROR_INVALID_VALUE;
+    if (!aligned(q_idx, 16) || !aligned(kidx_cache, 16) || !aligned(q, 16) ||
+        !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4) ||
+        !aligned(seq_lens, 4) || !aligned(cu_q, 4) || !aligned(out, 16) ||
+        (lse && !aligned(lse, 4)) || (sel && !aligned(sel, 4)))
+        return MSA_ERROR_INVALID_VALUE;
+    if ((int64_t)s.B * s.Hidx > 65535) return MSA_ERROR_NOT_SUPPORTED;
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < msa_multi_query_ws_bytes(s, total_q))
+        return MSA_ERROR_WORKSPACE;
+    return launched(msa_launch_multi_query_step(s, total_q, q_idx, kidx_cache, q, k_cache, v_cache,
+                                                block_table, seq_lens, cu_q, out, lse, sel,
+                                                workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t msa_decode_step_workspace_size(const msa_dims_t* dims) {
     MsaShape s;
     if (check_dims(dims, &s) != MSA_SUCCESS) return 0;

@@ -150,6 +150,13 @@ hipError_t msa_launch_decode(const MsaShape& s, const uint16_t* q, const uint16_
                              const int32_t* row_lens, uint16_t* out, float* lse, void* ws,
                              hipStream_t st);
 size_t msa_prefill_ws_bytes(const MsaShape& s, int total_q);
+size_t msa_multi_query_ws_bytes(const MsaShape& s, int total_q);
+hipError_t msa_launch_multi_query_step(const MsaShape& s, int total_q, const uint16_t* q_idx,
+                                       const uint16_t* kidx, const uint16_t* q,
+                                       const uint16_t* k_cache, const uint16_t* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* cu_q, uint16_t* out, float* lse,
+                                       int32_t* sel_out, void* ws, hipStream_t st);
 hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                               const uint16_t* k_cache, const uint16_t* v_cache,
                               const int32_t* block_table, const int32_t* seq_lens,

@@ -32,6 +32,7 @@
 
 #include "decode_tile.hpp"
 #include "msa_common.hpp"
+#include "select.hpp"
 
 namespace msa {
 namespace {
@@ -924,11 +925,17 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 // workgroup's blocks are looked up together, in one round trip.  (Loading a
 // block's K and V during the previous block's products gains nothing: the
 // query rows each pass loads wait behind those loads.)
+// With SELECT (the multi-query step) the workgroup first makes the top-k
+// selection of its queries itself from their block scores, one query per
+// wavefront at a time, with the selection rule of msa_topk_blocks (NPT
+// candidates per lane, one wavefront per row); stripe 0 publishes them in
+// sel.  Without it the selection is read from sel.
 constexpr int kMqEntries = 1024;                        // queries of a sequence x k, at most
 constexpr int kMqPerThread = kMqEntries / kDecThreads;  // entries held per thread
 constexpr int kMqMaxOwn = 128;                          // blocks per workgroup, at most
 constexpr int kMqMaxWords = kBlock * kHeadDim / 2;      // bitmap words the V tile holds
 
+template <bool SELECT, int NPT>
 __global__ __launch_bounds__(kDecThreads)
 void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                      const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
@@ -936,9 +943,11 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                      const int32_t* __restrict__ block_table,
                      const int32_t* __restrict__ seq_lens,
                      const int32_t* __restrict__ cu_q,
-                     const int32_t* __restrict__ sel,       // [T, Hkv, k]
+                     int32_t* __restrict__ sel,             // [T, Hkv, k]: read, or written with SELECT
+                     const float* __restrict__ scores,      // [T, Hkv, maxblk] (SELECT only)
                      PrefillWs w, int Hq, int Hkv, int maxblk, int P, float scale_log2) {
     __shared__ __attribute__((aligned(16))) DecodeShared sh;
+    __shared__ int32_t rsel[SELECT ? kMqEntries : 1];  // this (sequence, group)'s selections
     __shared__ uint16_t rows[kMqEntries];  // entry indices of the current block's rows
     __shared__ int own[kMqMaxOwn];         // this workgroup's blocks, in rank order
     __shared__ int own_page[kMqMaxOwn];    // their physical pages
@@ -954,13 +963,39 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int nq = cu_q[s + 1] - t0;
     const int n_e = min(nq * kTopK, kMqEntries);  // the host takes this kernel only when
                                                   // every sequence's entries fit
+    const int L = seq_lens[s];
+    const int pos0 = L - nq - t0;  // position of query token t: pos0 + t
+
+    if constexpr (SELECT) {
+        // query t0 + i of this (sequence, group) by wavefront i mod 4; the
+        // selection scratch lives in the V tile, free until the bitmap
+        static_assert(4 * sizeof(SelectShared<1>) <= sizeof(sh.vs), "selection scratch");
+        SelectShared<1>* ssh = reinterpret_cast<SelectShared<1>*>(sh.vs) + wave;
+        const int nq_sel = min(nq, kMqEntries / kTopK);
+        for (int i = wave; i < nq_sel; i += kDecThreads / kWave) {
+            const int t = t0 + i;
+            float raw[NPT];
+            int pg[NPT];
+            load_candidates<NPT, 1, false>(scores + ((size_t)t * Hkv + g) * maxblk, nullptr, maxblk,
+                                           0, lane, raw, pg);
+            select_row<NPT, 1>(raw, pg, (pos0 + t) / kBlock, 0, lane, ssh,
+                               [&](int pos, uint32_t, int b, int) {
+                                   rsel[i * kTopK + pos] = b;
+                                   if (p == 0) sel[((size_t)t * Hkv + g) * kTopK + pos] = b;
+                               });
+            wave_sync_lds();  // this wavefront's scratch is reused by its next query
+        }
+        __syncthreads();  // rsel complete; the selection scratch is free
+    }
 
     // entry e = q_local k + slot of this thread: tid + 256 i; its block, or -1
     int eb[kMqPerThread];
 #pragma unroll
     for (int i = 0; i < kMqPerThread; ++i) {
         const int e = tid + kDecThreads * i;
-        const int b = e < n_e ? sel[((size_t)(t0 + e / kTopK) * Hkv + g) * kTopK + e % kTopK] : -1;
+        int b = -1;
+        if (e < n_e)
+            b = SELECT ? rsel[e] : sel[((size_t)(t0 + e / kTopK) * Hkv + g) * kTopK + e % kTopK];
         eb[i] = (b >= 0 && b < maxblk) ? b : -1;
     }
     uint32_t* bits = reinterpret_cast<uint32_t*>(sh.vs);
@@ -1007,8 +1042,6 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     if (tid < n_own) own_page[tid] = block_table[(size_t)s * maxblk + own[tid]];
     __syncthreads();
 
-    const int L = seq_lens[s];
-    const int pos0 = L - nq - t0;  // position of query token t: pos0 + t
     auto nv_of = [&](int b) { return min(kBlock, L - b * kBlock); };
     auto load_own = [&](int j, SmallRaw& r) {
         const size_t page_off = ((size_t)own_page[j] * Hkv + g) * kBlock * kHeadDim;
@@ -1138,9 +1171,10 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
         const int u_avg = std::min(s.maxblk, ceil_div(total_q, s.B) * kTopK);
         const int u_max = std::min(s.maxblk, total_q * kTopK);
         const int P = std::max({1, ceil_div(u_avg, 8), ceil_div(u_max, kMqMaxOwn)});
-        hipLaunchKernelGGL(mq_block_kernel, dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0, st, q,
-                           k_cache, v_cache, block_table, seq_lens, cu_q, sel, w, s.Hq, s.Hkv,
-                           s.maxblk, P, s.scale * kLog2e);
+        hipLaunchKernelGGL((mq_block_kernel<false, 1>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
+                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                           const_cast<int32_t*>(sel), nullptr, w, s.Hq, s.Hkv, s.maxblk, P,
+                           s.scale * kLog2e);
         const int nth = total_q * s.Hq * 16;
         hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel,
                            w, out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
@@ -1171,6 +1205,63 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     hipLaunchKernelGGL(bucket_small_kernel, dim3(n_bk), dim3(kDecThreads), 0, st, q, k_cache,
                        v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
+    const int nth = total_q * s.Hq * 16;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
+                       out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
+    return hipGetLastError();
+}
+
+// The multi-query step's workspace: block scores [T, Hkv, maxblk] fp32, the
+// selection [T, Hkv, k] (used when the caller passes none), then the prefill
+// workspace.
+size_t msa_multi_query_ws_bytes(const MsaShape& s, int total_q) {
+    using namespace msa;
+    return align256((size_t)total_q * s.Hkv * s.maxblk * 4) +
+           align256((size_t)total_q * s.Hkv * kTopK * 4) + msa_prefill_ws_bytes(s, total_q);
+}
+
+hipError_t msa_launch_multi_query_step(const MsaShape& s, int total_q, const uint16_t* q_idx,
+                                       const uint16_t* kidx, const uint16_t* q,
+                                       const uint16_t* k_cache, const uint16_t* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* cu_q, uint16_t* out, float* lse,
+                                       int32_t* sel_out, void* ws, hipStream_t st) {
+    using namespace msa;
+    if (total_q == 0) return hipSuccess;
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base);
+    base += align256((size_t)total_q * s.Hkv * s.maxblk * 4);
+    int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(base);
+    base += align256((size_t)total_q * s.Hkv * kTopK * 4);
+    hipError_t e = msa_launch_index_score(s, total_q, q_idx, kidx, block_table, seq_lens, cu_q,
+                                          scores, st);
+    if (e != hipSuccess) return e;
+    // The attention kernel makes the selections itself when each wavefront
+    // selects about one query: every stripe of a (sequence, group) repeats
+    // them, which at 8 x 60k cost more than the separate selection launch with
+    // 8 drafts per sequence (104.7 against 100.5 us) and saved it with 4
+    // (64.8 against 66.7 us).
+    const bool fused = (int64_t)total_q * kTopK <= kMqEntries && total_q <= 4 * s.B &&
+                       s.maxblk <= 16 * kWave && ceil_div(s.maxblk, 32) <= kMqMaxWords;
+    if (!fused) {  // the three calls: selection, then the prefill entry's own form
+        e = msa_launch_topk(s, total_q, scores, seq_lens, cu_q, sel, st);
+        if (e != hipSuccess) return e;
+        return msa_launch_prefill(s, total_q, q, k_cache, v_cache, block_table, seq_lens, cu_q,
+                                  sel, out, lse, base, st);
+    }
+    PrefillWs w = prefill_ws(base, s.B, s.Hkv, s.maxblk, total_q, s.Hq);
+    // stripes as in msa_launch_prefill's multi-query form
+    const int u_avg = std::min(s.maxblk, ceil_div(total_q, s.B) * kTopK);
+    const int u_max = std::min(s.maxblk, total_q * kTopK);
+    const int P = std::max({1, ceil_div(u_avg, 8), ceil_div(u_max, kMqMaxOwn)});
+    if (s.maxblk <= 8 * kWave)
+        hipLaunchKernelGGL((mq_block_kernel<true, 8>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
+                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, scores, w,
+                           s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
+    else
+        hipLaunchKernelGGL((mq_block_kernel<true, 16>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
+                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, scores, w,
+                           s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
     const int nth = total_q * s.Hq * 16;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
                        out, lse, total_q, s.Hq, s.Hkv, s.maxblk);

@@ -2,7 +2,8 @@
 
 Decode:  msa_index_score -> msa_topk_blocks -> msa_build_page_table ->
          msa_sparse_attn_decode, or the fused msa_decode_step (same results).
-Prefill: msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill.
+Prefill: msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill, or the
+         one msa_multi_query_step call (same results).
 This module only allocates the outputs and the workspace (torch device memory)
 and calls the library; every step of the computation runs in its kernels.
 """
@@ -14,9 +15,11 @@ from . import _lib as L
 
 
 class MsaStep:
-    def __init__(self, x, lse: bool = True, fused: bool = False, prefill: bool = False):
+    def __init__(self, x, lse: bool = True, fused: bool = False, prefill: bool = False,
+                 multi: bool = False):
         """fused: the decode step as one msa_decode_step call; prefill: take the
-        prefill entry point even when every sequence has a single query."""
+        prefill entry point even when every sequence has a single query; multi:
+        the prefill path as one msa_multi_query_step call."""
         cfg = x.cfg
         self.x = x
         self.cfg = cfg
@@ -29,8 +32,11 @@ class MsaStep:
         self.out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, cfg.num_q_heads), dtype=torch.float32, device=dev) if lse else None
         self.fused = fused and self.decode
+        self.multi = multi and not self.decode
         if self.fused:
             nbytes = L.msa_decode_step_workspace_size(self.dims)
+        elif self.multi:
+            nbytes = L.msa_multi_query_step_workspace_size(self.dims, T)
         elif self.decode:
             R = cfg.num_seqs * H
             self.page_table = torch.empty((R, cfg.topk), dtype=torch.int32, device=dev)
@@ -53,6 +59,11 @@ class MsaStep:
                                                     x.k_cache, x.v_cache, x.block_table,
                                                     x.seq_lens, self.out, self.lse, self.sel,
                                                     self.workspace)
+        elif self.multi:
+            self._fused = L.prepare_msa_multi_query_step(self.dims, T, x.q_idx, x.kidx_cache, x.q,
+                                                         x.k_cache, x.v_cache, x.block_table,
+                                                         x.seq_lens, x.cu_q, self.out, self.lse,
+                                                         self.sel, self.workspace)
         elif self.decode:
             self._page_table = L.prepare_msa_build_page_table(self.dims, self.sel, x.block_table,
                                                               x.seq_lens, self.page_table,
@@ -82,7 +93,7 @@ class MsaStep:
         self._fused(stream)
 
     def run(self, stream=None):
-        if self.fused:
+        if self.fused or self.multi:
             self.fused_step(stream)
             return self.out
         self.score(stream)

@@ -17,6 +17,10 @@
  *   [mechatronic] "MiniMax M3: MoE de 428B con 1M de contexto en Blackwell",
  *                 section on what makes M3 different (each KV block read once,
  *                 contiguously; attention on real KV).
+ *   [despertar]   despertarmatinal.com page on MiniMax M2 and M3 -- the
+ *                 paragraph on the multi-token prediction (MTP) modules used
+ *                 for speculative decoding, and the section "MiniMax Sparse
+ *                 Attention (MSA) y escalado subcuadratico entrante".
  * The pages do not give the scoring function.  This library fixes it as:
  * score(block) = max over the block's causally visible tokens of
  * q_idx . k_idx (idx_dim = 64, fp32 accumulation); blocks after the query's
@@ -227,6 +231,41 @@ msa_status_t msa_decode_step_noalloc(const msa_dims_t *dims, const uint16_t *q_i
                                      uint16_t *out, float *lse, int32_t *sel, void *stream);
 
 /*
+ * A multi-query layer-step: a few query tokens per sequence, e.g. the draft
+ * tokens of speculative decoding ([despertar] paragraph on the multi-token
+ * prediction (MTP) modules used for speculative decoding), each KV block read
+ * once for all of a sequence's drafts ([aivizor] KV-Block-Major paragraph).
+ * Same results as msa_index_score,
+ * msa_topk_blocks and msa_sparse_attn_prefill called in turn, bit for bit.
+ *
+ * With at most 4 queries per sequence on average, total_q x k <= 1024 and
+ * max_blocks_per_seq <= 1024 it runs in three launches:
+ *   - scoring, as msa_index_score;
+ *   - one kernel whose (sequence, group) workgroups make the top-k selection
+ *     of their sequence's queries from the scores (the rule of
+ *     msa_topk_blocks), find the union of the selected blocks and attend
+ *     each block once for every query that selected it;
+ *   - the Log-Sum-Exp merge.
+ * Otherwise it makes the three calls' own launches.
+ *
+ * Arguments:
+ *   q_idx [total_q, H_kv, 64] and q [total_q, H_q, 128] bf16; caches,
+ *         block_table, seq_lens, cu_q as for the prefill calls (query token t
+ *         of sequence s at position seq_lens[s] - n_s + (t - cu_q[s]))
+ *   out   [total_q, H_q, 128] bf16 (output); lse [total_q, H_q] fp32 or NULL
+ *   sel   [total_q, H_kv, k] int32 (output, the selection) or NULL
+ *   workspace: at least msa_multi_query_step_workspace_size(dims, total_q)
+ *         bytes, 256-byte aligned; no initial contents required.
+ */
+msa_status_t msa_multi_query_step(const msa_dims_t *dims, int32_t total_q, const uint16_t *q_idx,
+                                  const uint16_t *kidx_cache, const uint16_t *q,
+                                  const uint16_t *k_cache, const uint16_t *v_cache,
+                                  const int32_t *block_table, const int32_t *seq_lens,
+                                  const int32_t *cu_q, uint16_t *out, float *lse, int32_t *sel,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dense GQA decode attention, the baseline MSA's decode speedup is measured/*
  * Dense GQA decode attention, the baseline MSA's decode speedup is measured
  * against ([youmind] bullet "Rapido en produccion": decode vs dense GQA with
  * the same heads): every query head of sequence s attends all seq_lens[s]
@@ -325,6 +364,7 @@ msa_status_t msa_validate_inputs(const msa_dims_t *dims, int32_t total_q,
 size_t msa_decode_workspace_size(const msa_dims_t *dims);
 size_t msa_prefill_workspace_size(const msa_dims_t *dims, int32_t total_q);
 size_t msa_decode_step_workspace_size(const msa_dims_t *dims);
+size_t msa_multi_query_step_workspace_size(const msa_dims_t *dims, int32_t total_q);
 size_t msa_dense_decode_workspace_size(const msa_dims_t *dims);
 
 /* Static, human-readable name of a status code. */

@@ -234,3 +234,27 @@ def test_decode_step_noalloc_host_checks():
                                        N) == L.MSA_ERROR_WORKSPACE
     assert lib.msa_decode_step_noalloc(ctypes.byref(dims(head_dim=64)), A, A, A, A, A, A, A, A, A,
                                        A, N) == L.MSA_ERROR_NOT_SUPPORTED
+
+
+def test_multi_query_step_host_checks():
+    """msa_multi_query_step: no queries succeeds without pointers; NULL or
+    misaligned pointers and a short workspace are refused before any HIP call;
+    the workspace covers the block scores, a selection and the prefill
+    workspace."""
+    lib = L.lib()
+    N = None
+    d = dims()
+    assert lib.msa_multi_query_step(ctypes.byref(d), 0, N, N, N, N, N, N, N, N, N, N, N, N, 0,
+                                    N) == L.MSA_SUCCESS
+    assert lib.msa_multi_query_step(ctypes.byref(d), -1, A, A, A, A, A, A, A, A, A, N, N, A,
+                                    1 << 30, N) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_multi_query_step(ctypes.byref(d), 4, N, A, A, A, A, A, A, A, A, N, N, A,
+                                    1 << 30, N) == L.MSA_ERROR_INVALID_VALUE
+    assert lib.msa_multi_query_step(ctypes.byref(d), 4, A, A, A, A, A, A, A, MIS, A, N, N, A,
+                                    1 << 30, N) == L.MSA_ERROR_INVALID_VALUE
+    need = L.msa_multi_query_step_workspace_size(d, 4)
+    T, H, W = 4, d.num_kv_heads, d.max_blocks_per_seq
+    assert need >= T * H * W * 4 + T * H * 16 * 4 + L.msa_prefill_workspace_size(d, 4)
+    assert lib.msa_multi_query_step(ctypes.byref(d), 4, A, A, A, A, A, A, A, A, A, N, N, A,
+                                    need - 256, N) == L.MSA_ERROR_WORKSPACE
+    assert L.msa_multi_query_step_workspace_size(dims(head_dim=64), 4) == 0

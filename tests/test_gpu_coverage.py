@@ -173,3 +173,38 @@ def test_multi_query_kernel(cfg):
     selection and every attention row against the oracle, padding poisoned."""
     print(f"[mq] {cfg.name} T={cfg.total_q} maxblk={cfg.max_blocks}", flush=True)
     parity.full_check(cfg, poison=True, attn_rows=cfg.total_q * cfg.num_q_heads)
+
+
+MQ_STEP = MQ + [
+    # the step's own selection with a wavefront selecting two queries of the
+    # 7-draft sequence (at most 4 queries per sequence on average)
+    gen.MsaConfig("mq_step_skewed", [30_000, 9_000, 5_000, 700], [7, 1, 2, 1], 48, 8,
+                  permute_pages=True, seed=107),
+    # 513..1024 blocks: 16 candidates per lane in the step's own selection
+    gen.MsaConfig("mq_782_blocks", [100_000, 70_000, 3_000], [3, 2, 4], 24, 4, permute_pages=True,
+                  seed=106),
+    gen.MsaConfig("multi_query_decode", [9000, 20000, 3000, 700], [4, 4, 2, 3], 12, 3,
+                  permute_pages=True, seed=48),
+]
+
+
+@pytest.mark.parametrize("cfg", MQ_STEP, ids=lambda c: c.name)
+def test_multi_query_step_equals_the_three_calls(cfg):
+    """msa_multi_query_step (its own in-kernel selection with at most 4 queries
+    per sequence on average, T x k <= 1024 and rows at most 1024 blocks wide,
+    else the three calls' launches)
+    against msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill, bit
+    for bit: outputs, log-sum-exps and the selection; run twice."""
+    print(f"[mq step] {cfg.name} T={cfg.total_q} maxblk={cfg.max_blocks}", flush=True)
+    x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
+    ref = MsaStep(x)
+    ref.run()
+    step = MsaStep(x, multi=True)
+    for _ in range(2):
+        step.sel.fill_(-7)
+        step.out.fill_(0)
+        step.run()
+        torch.cuda.synchronize()
+        assert torch.equal(step.sel, ref.sel)
+        assert torch.equal(step.out, ref.out)
+        assert torch.equal(step.lse, ref.lse)

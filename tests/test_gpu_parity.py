@@ -42,6 +42,10 @@ SMALL = [
     # blocks), G = 1 (buckets of up to 32 queries are small)
     gen.MsaConfig("prefill_from_scratch_g1", [1500, 300, 2600], [1500, 300, 2600], 4, 4,
                   permute_pages=True, seed=59),
+    # more than 128 new tokens per sequence on average: the GEMM scoring form,
+    # row groups of several sequences' queries, one sequence with none
+    gen.MsaConfig("prefill_gemm_mixed", [3000, 900, 5000], [600, 0, 800], 12, 4,
+                  permute_pages=True, seed=60),
 ]
 
 
@@ -97,7 +101,7 @@ def test_small_cases_poisoned_padding(cfg):
     parity.full_check(cfg, poison=True)
 
 
-@pytest.mark.parametrize("cfg", SMALL[:1] + SMALL[4:5], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", SMALL[:1] + SMALL[4:5] + SMALL[8:10], ids=lambda c: c.name)
 def test_per_group_index_keys(cfg):
     parity.full_check(cfg.with_idx_heads(cfg.num_kv_heads), poison=True)
 
