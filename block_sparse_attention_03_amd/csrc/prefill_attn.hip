@@ -930,12 +930,27 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 // wavefront at a time, with the selection rule of msa_topk_blocks (NPT
 // candidates per lane, one wavefront per row); stripe 0 publishes them in
 // sel.  Without it the selection is read from sel.
-constexpr int kMqEntries = 1024;                        // queries of a sequence x k, at most
-constexpr int kMqPerThread = kMqEntries / kDecThreads;  // entries held per thread
+constexpr int kMqEntries = 4096;                        // queries of a sequence x k, at most
+// The kernel is compiled for 1,024 entries too, used when the call's entries
+// fit: fewer registers and LDS (at 8 x 60k with 4 and 8 drafts, 65.2 and
+// 103.2 us per step against 65.8 and 104.4 us).
+constexpr int kMqSmallEntries = 1024;
 constexpr int kMqMaxOwn = 128;                          // blocks per workgroup, at most
 constexpr int kMqMaxWords = kBlock * kHeadDim / 2;      // bitmap words the V tile holds
 
-template <bool SELECT, int NPT>
+// The multi-query form serves calls whose every sequence's entries fit
+// (total_q x k <= kMqEntries) with at most 32 queries per sequence on
+// average.  Past that, blocks are chosen by enough of a sequence's queries
+// that the inverse map and the block-major kernel win: at 60k, one sequence
+// with 128 or 256 new tokens took 187 and 332 us in this form against 180
+// and 306 us, while 8 sequences with 16 or 32 drafts each took 149 and 211
+// us against 167 and 235 us.
+inline bool mq_form(const MsaShape& s, int total_q) {
+    return (int64_t)total_q * kTopK <= kMqEntries && total_q <= 32 * s.B &&
+           ceil_div(s.maxblk, 32) <= kMqMaxWords;
+}
+
+template <bool SELECT, int NPT, int CAP>
 __global__ __launch_bounds__(kDecThreads)
 void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                      const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
@@ -947,8 +962,9 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                      const float* __restrict__ scores,      // [T, Hkv, maxblk] (SELECT only)
                      PrefillWs w, int Hq, int Hkv, int maxblk, int P, float scale_log2) {
     __shared__ __attribute__((aligned(16))) DecodeShared sh;
-    __shared__ int32_t rsel[SELECT ? kMqEntries : 1];  // this (sequence, group)'s selections
-    __shared__ uint16_t rows[kMqEntries];  // entry indices of the current block's rows
+    constexpr int kMqPerThread = CAP / kDecThreads;  // entries held per thread
+    __shared__ int32_t rsel[SELECT ? CAP : 1];  // this (sequence, group)'s selections
+    __shared__ uint16_t rows[CAP];  // entry indices of the current block's rows
     __shared__ int own[kMqMaxOwn];         // this workgroup's blocks, in rank order
     __shared__ int own_page[kMqMaxOwn];    // their physical pages
     __shared__ int wtot[kDecThreads / kWave];
@@ -961,7 +977,7 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int G = Hq / Hkv;
     const int t0 = cu_q[s];
     const int nq = cu_q[s + 1] - t0;
-    const int n_e = min(nq * kTopK, kMqEntries);  // the host takes this kernel only when
+    const int n_e = min(nq * kTopK, CAP);  // the host takes this kernel only when
                                                   // every sequence's entries fit
     const int L = seq_lens[s];
     const int pos0 = L - nq - t0;  // position of query token t: pos0 + t
@@ -971,7 +987,7 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         // selection scratch lives in the V tile, free until the bitmap
         static_assert(4 * sizeof(SelectShared<1>) <= sizeof(sh.vs), "selection scratch");
         SelectShared<1>* ssh = reinterpret_cast<SelectShared<1>*>(sh.vs) + wave;
-        const int nq_sel = min(nq, kMqEntries / kTopK);
+        const int nq_sel = min(nq, CAP / kTopK);
         for (int i = wave; i < nq_sel; i += kDecThreads / kWave) {
             const int t = t0 + i;
             float raw[NPT];
@@ -1159,7 +1175,7 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     const size_t map_lds = (size_t)s.maxblk * sizeof(int32_t);
     // buckets of at most small_cnt entries (kSmallRows rows) are small
     const int small_cnt = kSmallRows / (s.Hq / s.Hkv);
-    if ((int64_t)total_q * kTopK <= kMqEntries && ceil_div(s.maxblk, 32) <= kMqMaxWords) {
+    if (mq_form(s, total_q)) {
         // a few queries per sequence: one kernel finds each (sequence, group)'s
         // blocks and attends them.  P workgroups per (sequence, group): about
         // eight blocks each when the queries are spread evenly over the
@@ -1171,10 +1187,15 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
         const int u_avg = std::min(s.maxblk, ceil_div(total_q, s.B) * kTopK);
         const int u_max = std::min(s.maxblk, total_q * kTopK);
         const int P = std::max({1, ceil_div(u_avg, 8), ceil_div(u_max, kMqMaxOwn)});
-        hipLaunchKernelGGL((mq_block_kernel<false, 1>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
-                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q,
-                           const_cast<int32_t*>(sel), nullptr, w, s.Hq, s.Hkv, s.maxblk, P,
-                           s.scale * kLog2e);
+        int32_t* sel_rw = const_cast<int32_t*>(sel);  // read only: no selection in this form
+        if ((int64_t)total_q * kTopK <= kMqSmallEntries)
+            hipLaunchKernelGGL((mq_block_kernel<false, 1, kMqSmallEntries>), dim3(s.B * s.Hkv, P),
+                               dim3(kDecThreads), 0, st, q, k_cache, v_cache, block_table, seq_lens,
+                               cu_q, sel_rw, nullptr, w, s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
+        else
+            hipLaunchKernelGGL((mq_block_kernel<false, 1, kMqEntries>), dim3(s.B * s.Hkv, P),
+                               dim3(kDecThreads), 0, st, q, k_cache, v_cache, block_table, seq_lens,
+                               cu_q, sel_rw, nullptr, w, s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
         const int nth = total_q * s.Hq * 16;
         hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel,
                            w, out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
@@ -1241,8 +1262,7 @@ hipError_t msa_launch_multi_query_step(const MsaShape& s, int total_q, const uin
     // them, which at 8 x 60k cost more than the separate selection launch with
     // 8 drafts per sequence (104.7 against 100.5 us) and saved it with 4
     // (64.8 against 66.7 us).
-    const bool fused = (int64_t)total_q * kTopK <= kMqEntries && total_q <= 4 * s.B &&
-                       s.maxblk <= 16 * kWave && ceil_div(s.maxblk, 32) <= kMqMaxWords;
+    const bool fused = mq_form(s, total_q) && total_q <= 4 * s.B && s.maxblk <= 16 * kWave;
     if (!fused) {  // the three calls: selection, then the prefill entry's own form
         e = msa_launch_topk(s, total_q, scores, seq_lens, cu_q, sel, st);
         if (e != hipSuccess) return e;
@@ -1254,14 +1274,19 @@ hipError_t msa_launch_multi_query_step(const MsaShape& s, int total_q, const uin
     const int u_avg = std::min(s.maxblk, ceil_div(total_q, s.B) * kTopK);
     const int u_max = std::min(s.maxblk, total_q * kTopK);
     const int P = std::max({1, ceil_div(u_avg, 8), ceil_div(u_max, kMqMaxOwn)});
-    if (s.maxblk <= 8 * kWave)
-        hipLaunchKernelGGL((mq_block_kernel<true, 8>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
-                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, scores, w,
-                           s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
-    else
-        hipLaunchKernelGGL((mq_block_kernel<true, 16>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), 0,
-                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, scores, w,
-                           s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
+#define MSA_MQ(NPT, CAP)                                                                       \
+    hipLaunchKernelGGL((mq_block_kernel<true, NPT, CAP>), dim3(s.B * s.Hkv, P), dim3(kDecThreads), \
+                       0, st, q, k_cache, v_cache, block_table, seq_lens, cu_q, sel, scores, w,   \
+                       s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e)
+    const bool small = (int64_t)total_q * kTopK <= kMqSmallEntries;
+    if (s.maxblk <= 8 * kWave) {
+        if (small) MSA_MQ(8, kMqSmallEntries);
+        else MSA_MQ(8, kMqEntries);
+    } else {
+        if (small) MSA_MQ(16, kMqSmallEntries);
+        else MSA_MQ(16, kMqEntries);
+    }
+#undef MSA_MQ
     const int nth = total_q * s.Hq * 16;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
                        out, lse, total_q, s.Hq, s.Hkv, s.maxblk);

@@ -238,7 +238,7 @@ msa_status_t msa_decode_step_noalloc(const msa_dims_t *dims, const uint16_t *q_i
  * Same results as msa_index_score,
  * msa_topk_blocks and msa_sparse_attn_prefill called in turn, bit for bit.
  *
- * With at most 4 queries per sequence on average, total_q x k <= 1024 and
+ * With at most 4 queries per sequence on average, total_q x k <= 4096 and
  * max_blocks_per_seq <= 1024 it runs in three launches:
  *   - scoring, as msa_index_score;
  *   - one kernel whose (sequence, group) workgroups make the top-k selection

@@ -24,13 +24,14 @@ page workgroups fit on the chip at once (R <= 64), else 2, 4 or 8
 (decode_multi_kernel<NPT, W, PAGES, slots>: R < 128, R < 256, R >= 256).
 MULTI covers each of those with short and long rows.
 
-msa_sparse_attn_prefill picks its form by the number of queries T and the
-row width: with T x k <= 1024 (a few draft tokens per sequence)
-mq_block_kernel finds each (sequence, group)'s union of selected blocks itself
-and attends each block once for all the drafts that chose it; otherwise an
-inverse map (one workgroup while the buckets and selections are few, else
-four kernels) feeds the block-major kernel (buckets of more than 32 rows) and
-the small-bucket kernel.  MQ covers the first form's limits and the switch.
+msa_sparse_attn_prefill picks its form by the number of queries T, the
+batch size B and the row width: with T x k <= 4096 and T <= 32 B (draft
+tokens, a few dozen per sequence at most) mq_block_kernel finds each
+(sequence, group)'s union of selected blocks itself and attends each block
+once for all the queries that chose it; otherwise an inverse map (one
+workgroup while the buckets and selections are few, else four kernels) feeds
+the block-major kernel (buckets of more than 32 rows) and the small-bucket
+kernel.  MQ covers the first form's limits and both switches.
 """
 import numpy as np
 import pytest
@@ -155,10 +156,19 @@ MQ = [
     # of about eight blocks), a sequence with none
     gen.MsaConfig("mq_skewed_64", [30_000, 9_000, 5_000, 700], [60, 0, 3, 1], 48, 8,
                   permute_pages=True, seed=101),
-    # exactly 64 queries in one sequence: every entry slot of the kernel used
-    gen.MsaConfig("mq_one_seq_64", [16_000], [64], 16, 2, permute_pages=True, seed=102),
-    # 65 queries: past the kernel's limit, the one-workgroup inverse map
-    gen.MsaConfig("mq_one_seq_65", [16_000], [65], 16, 2, permute_pages=True, seed=103),
+    # 256 queries, all in one of 8 sequences (32 per sequence on average):
+    # every entry slot of the kernel used by that sequence's groups
+    gen.MsaConfig("mq_256_in_one_of_8", [20_000] + [3_000] * 7, [256] + [0] * 7, 16, 2,
+                  permute_pages=True, seed=102),
+    # 257 queries: past the kernel's entries, the one-workgroup inverse map
+    gen.MsaConfig("mq_257_in_one_of_8", [20_000] + [3_000] * 7, [257] + [0] * 7, 16, 2,
+                  permute_pages=True, seed=103),
+    # 33 queries per sequence on average: the inverse map and bucket kernels
+    gen.MsaConfig("mq_33_per_sequence", [16_000, 9_000], [33, 33], 16, 2, permute_pages=True,
+                  seed=108),
+    # 32 per sequence: still the multi-query kernel
+    gen.MsaConfig("mq_32_per_sequence", [16_000, 9_000], [32, 32], 16, 2, permute_pages=True,
+                  seed=109),
     # G = 1, drafts of several lengths
     gen.MsaConfig("mq_g1", [5_000, 12_000, 800], [4, 7, 2], 4, 4, permute_pages=True, seed=104),
     # a 2,097,152-token row (16,384 blocks: two bitmap words per thread)
@@ -176,6 +186,12 @@ def test_multi_query_kernel(cfg):
 
 
 MQ_STEP = MQ + [
+    # more than 64 query tokens with at most 4 per sequence: the step's own
+    # selection in the 4,096-entry kernel, 8 and 16 candidates per lane
+    gen.MsaConfig("mq_step_20_seqs", _lens(20, 2_000, 20_000, 5), [4] * 20, 16, 2,
+                  permute_pages=True, seed=110),
+    gen.MsaConfig("mq_step_20_seqs_100k", [100_000] + _lens(19, 2_000, 9_000, 6), [4] * 20, 16, 2,
+                  permute_pages=True, seed=111),
     # the step's own selection with a wavefront selecting two queries of the
     # 7-draft sequence (at most 4 queries per sequence on average)
     gen.MsaConfig("mq_step_skewed", [30_000, 9_000, 5_000, 700], [7, 1, 2, 1], 48, 8,
@@ -191,7 +207,7 @@ MQ_STEP = MQ + [
 @pytest.mark.parametrize("cfg", MQ_STEP, ids=lambda c: c.name)
 def test_multi_query_step_equals_the_three_calls(cfg):
     """msa_multi_query_step (its own in-kernel selection with at most 4 queries
-    per sequence on average, T x k <= 1024 and rows at most 1024 blocks wide,
+    per sequence on average, T x k <= 4096 and rows at most 1024 blocks wide,
     else the three calls' launches)
     against msa_index_score -> msa_topk_blocks -> msa_sparse_attn_prefill, bit
     for bit: outputs, log-sum-exps and the selection; run twice."""
