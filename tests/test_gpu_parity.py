@@ -240,6 +240,23 @@ def test_chunked_prefill_64k():
           f"lse max abs {l_err:.3g})", flush=True)
 
 
+@pytest.mark.parametrize("drafts", [4, 8])
+def test_multi_query_decode_60k(drafts):
+    """The bench's multi-query workloads at full size (8 x 60k, 4 or 8 draft
+    tokens per sequence, padding poisoned): the three calls against the
+    oracle (every score row, selection and attention row), and
+    msa_multi_query_step bit-equal to them."""
+    import dataclasses
+    cfg = dataclasses.replace(gen.config(2), name=f"mq_60k_{drafts}drafts", n_new=[drafts] * 8)
+    x, step = parity.full_check(cfg, poison=True, attn_rows=cfg.total_q * cfg.num_q_heads)
+    multi = MsaStep(x, multi=True)
+    multi.run()
+    torch.cuda.synchronize()
+    assert torch.equal(multi.sel, step.sel)
+    assert torch.equal(multi.out, step.out)
+    assert torch.equal(multi.lse, step.lse)
+
+
 def test_paged_decode_60k_per_group_index_keys():
     parity.full_check(gen.config(2).with_idx_heads(8), poison=True)
 
