@@ -900,10 +900,13 @@ def main():
         if want_cpu:
             cpu_cfg[c3.name] = cpu_stages(c3, l3[0], sample_queries=32)
         s3 = [MsaStep(x) for x in l3]
-        n3 = max(6, args.steps // 25)
-        ms3 = time_calls([s.run for s in s3], n3, 2)
-        score3 = time_calls([s.score for s in s3], n3, 2)
-        attn3 = time_calls([s.attend for s in s3], n3, 2)
+        n3 = max(8, args.steps // 25)
+        # enough untimed steps (about 15 ms) for the clocks to settle after the
+        # lighter decode workloads
+        w3 = max(8, args.warmup // 2)
+        ms3 = time_calls([s.run for s in s3], n3, w3)
+        score3 = time_calls([s.score for s in s3], n3, w3)
+        attn3 = time_calls([s.attend for s in s3], n3, w3)
         fl_attn, fl_score = acc.attn_flops(c3), acc.score_flops(c3)
         tf = lambda fl, ms_: fl / (ms_ * 1e-3) / 1e12
         also[c3.name] = {
