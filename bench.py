@@ -551,12 +551,15 @@ def record_traffic(name, copy_f, copy_w, fetch, write):
     print(json.dumps(rec))
 
 
-def measured_ceilings():
+def measured_ceilings(chain=None):
     """Sustained HBM read bandwidth and bf16 matrix-core rate on this GPU, from
     the separate calibration library: the best over a few grid sizes of a
     2 GiB streaming read; the same for 64 MiB reads (the size of one decode
     layer-step's two passes) cycling over 32 distinct slices; and independent
-    32x32x16 products at 4 and 8 waves per SIMD."""
+    32x32x16 products at 4 and 8 waves per SIMD.  With chain = (a, b, c)
+    bytes, also the time of three dependent contiguous reads of a, b and c
+    bytes, one launch each, back to back over distinct slices: the floor of
+    a three-launch decode step that streams those bytes."""
     import ctypes
     import os
     import torch
@@ -615,6 +618,20 @@ def measured_ceilings():
                 raise RuntimeError("msa_calib_copy_grid failed")
         ms = time_calls([cps], 40, 8)
         copy_small[grid] = 2 * small_half / (ms * 1e-3) / 1e9
+    chain_us = None
+    if chain:
+        sizes = [int(n) // 16 * 16 for n in chain]
+        span = sum(sizes)
+        grids = [max(sized, key=sized.get) if n > small // 4 else min(4096, -(-n // (16 * 256)))
+                 for n in sizes]
+
+        def chain_call(i):
+            off = base + i * span
+            for n, g in zip(sizes, grids):
+                read(off, n, g)
+                off += n
+        fns = [lambda i=i: chain_call(i) for i in range(nbytes // span)]
+        chain_us = time_calls(fns, 4 * len(fns), len(fns)) * 1e3
     tflops = {}
     for blocks in (1024, 2048):
         # enough warm-up launches (about 1 ms each) for the clocks to settle
@@ -627,7 +644,7 @@ def measured_ceilings():
     gb, gs, bm = max(big, key=big.get), max(sized, key=sized.get), max(tflops, key=tflops.get)
     gc = max(copy, key=copy.get)
     gcs = max(copy_small, key=copy_small.get)
-    return {"hbm_read_gbs": round(big[gb], 1),
+    res = {"hbm_read_gbs": round(big[gb], 1),
             "hbm_read_64mib_gbs": round(sized[gs], 1),
             "hbm_copy_800mib_gbs": round(copy[gc], 1),
             "copy_96mib_gbs": round(copy_small[gcs], 1),
@@ -642,6 +659,10 @@ def measured_ceilings():
                    f"per CU; torch.matmul (hipBLASLt) bf16 8192^3 on N(0,1) and on all-ones operands",
             "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
             "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
+    if chain_us is not None:
+        res["three_read_launches_us"] = round(chain_us, 2)
+        res["three_read_launches_bytes"] = [int(n) for n in chain]
+    return res
 
 
 def vendor_gemm_tflops():
@@ -800,8 +821,14 @@ def main():
     append_lines = {cfg.name: append_line(cfg, layers, args.steps, fused)}
     del fused, four, layers
     torch.cuda.empty_cache()
-    ceil = measured_ceilings()
+    # the step's streams as three plain dependent reads: index keys, the
+    # attended K/V (and q/out), the page partials the merge reads back
+    chain = (acc.score_bytes(cfg), acc.decode_attn_bytes(cfg),
+             cfg.total_q * cfg.num_q_heads * cfg.topk * (2 * cfg.head_dim + 4))
+    ceil = measured_ceilings(chain)
     result["measured_ceilings"] = ceil
+    result["layer_step"]["three_read_launches_over_step"] = round(
+        ceil["three_read_launches_us"] / (result["ms_per_step"] * 1e3), 4)
     result["roofline"]["frac_of_measured"] = round(
         result["roofline"]["achieved"] / ceil["hbm_read_gbs"], 4)
     result["roofline"]["frac_of_measured_64mib"] = round(
