@@ -193,14 +193,7 @@ void bucket_count_kernel(const int32_t* __restrict__ sel, const int32_t* __restr
     }
 }
 
-// Exclusive scan of counts[0..n) into offsets[0..n], one workgroup; it also
-// lists the nonempty buckets in order, those of more than small_cnt entries in
-// buckets and the others in small ([0] = how many, then their ids), so each
-// attention kernel launches only as many workgroups as there can be buckets
-// and none walks an empty one.  The counts go through in tiles of 8192: each
-// thread takes 8 consecutive buckets (two 16-byte loads), wavefront prefix
-// sums by lane shuffles, one LDS exchange of the 16 wavefront totals, and a
-// running carry from tile to tile.
+// Inclusive prefix sum of v over the lanes of the wavefront.
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
     const int lane = __lane_id();
 #pragma unroll
@@ -211,6 +204,14 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
+// Exclusive scan of counts[0..n) into offsets[0..n], one workgroup; it also
+// lists the nonempty buckets in order, those of more than small_cnt entries in
+// buckets and the others in small ([0] = how many, then their ids), so each
+// attention kernel launches only as many workgroups as there can be buckets
+// and none walks an empty one.  The counts go through in tiles of 8192: each
+// thread takes 8 consecutive buckets (two 16-byte loads), wavefront prefix
+// sums by lane shuffles, one LDS exchange of the 16 wavefront totals, and a
+// running carry from tile to tile.
 __global__ __launch_bounds__(1024)
 void scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                  int32_t* __restrict__ buckets, int32_t* __restrict__ small, int n,
@@ -488,7 +489,8 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                         int maxblk, float scale_log2) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[kBlock * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kVStride];
-    // per-wave staging of 32 query rows in, then 32 partial-output rows out
+    // per-wave staging of 32 partial-output rows: accumulator fragments in,
+    // whole 256-byte rows out as 16-byte stores
     __shared__ __attribute__((aligned(16))) uint16_t tiles[(kPfThreads / kWave) * 32 * kKStride];
 
     if ((int)blockIdx.x >= w.buckets[0]) return;  // uniform
@@ -542,8 +544,6 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     constexpr int kWaves = kPfThreads / kWave;
     uint16_t* tbuf = tiles + wave * 32 * kKStride;  // this wave's 32-row staging tile
 
-    // Row n of a tile: its query, head and selection slot.  Rows past the
-    // bucket repeat its last row (real data; results discarded).
     // Row n of a tile: its (query << 4 | slot) entry -- fetched two tiles
     // ahead -- and from it the query, head and slot.  Rows past the bucket
     // repeat its last row (real data; results discarded).
@@ -556,8 +556,6 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         *head_out = g * G + rho % G;
         return rho0 < nrows;
     };
-    // Coalesced gather of a tile's 32 query rows: instruction it moves rows
-    // 4it .. 4it+3, 16 lanes x 16 bytes each.
     // Direct gather of a tile's query rows into B operands: lane (n, h) loads
     // dims 64h + 8i .. +7 of its row n for k-step i.
     auto gather_q = [&](int t_n, int head_n, u32x4* raw) {
