@@ -126,6 +126,22 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
     __shared__ __attribute__((aligned(16))) u32x4 kstage[kScoreWaves][kBlock / 2 * 8];
     u32x4* st = kstage[wave];
     const u32x4* kb = reinterpret_cast<const u32x4*>(kidx + ((size_t)page * Hidx + ih) * kBlock * kIdxDim);
+    // B operands of rows r0 .. r0+15 (lane row m_in, dims 32i + 8kg .. +7;
+    // zero past the last row).  The first group's are loaded ahead of the
+    // keys, each later group's during the products of the one before, so no
+    // row waits for a query load after its keys arrive.
+    auto load_rows = [&](int r0, bf16x8 (&bq)[2]) {
+        const int rho = r0 + m_in;
+        const bool ok = rho < nrows;
+        const int qi = ok ? rho / R : 0;
+        const int g = (Hidx == 1) ? (ok ? rho % R : 0) : ih;
+        const uint16_t* qrow = q_idx + ((size_t)(q0 + qi) * Hkv + g) * kIdxDim;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            bq[i] = as_bf16x8(ok ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u});
+    };
+    bf16x8 bq_next[2];
+    load_rows(0, bq_next);
     u32x4 raw[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) raw[j] = ld16_stream(kb + kWave * j + lane);
@@ -167,13 +183,8 @@ void index_score_kernel(const uint16_t* __restrict__ q_idx,   // [T, Hkv, 64]
         const int t = q0 + qi;
         const int g = (Hidx == 1) ? (row_ok ? rho % R : 0) : ih;
         const int p = first_pos + qi;
-        bf16x8 bq[2];
-        const uint16_t* qrow = q_idx + ((size_t)t * Hkv + g) * kIdxDim;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            u32x4 v = row_ok ? ld16(qrow + 32 * i + 8 * kg) : u32x4{0u, 0u, 0u, 0u};
-            bq[i] = as_bf16x8(v);
-        }
+        const bf16x8 bq[2] = {bq_next[0], bq_next[1]};
+        if (r0 + 16 < nrows) load_rows(r0 + 16, bq_next);
         float best = -__builtin_inff();
         // tokens of this lane: tok0 + 16*mt + 4*kg + r; visible iff <= p
         const int lim = p - tok0 - 4 * kg;  // visible iff 16*mt + r <= lim
