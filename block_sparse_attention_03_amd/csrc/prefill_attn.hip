@@ -20,14 +20,18 @@
 //      O^T = V^T P^T, whose V^T operand comes from LDS transpose reads.  The
 //      next row tile's query gathers are issued before the current tile's
 //      softmax, hiding their latency.  Each (query, head, slot) gets a normalised bf16 partial
-//      output and an fp32 log-sum-exp;
+//      output and an fp32 log-sum-exp, stored in bucket order (a tile's 32 rows
+//      are consecutive: contiguous streaming stores, where rows placed by query
+//      would scatter 256-byte pieces), and the inverse map records where each
+//      selection's partials went;
 //      Buckets of at most 32 (query, head) rows -- a few queries per sequence,
 //      as in multi-query decode -- go to a lighter kernel instead: 256
 //      threads, each wavefront's 32 tokens of K held as 16x16x32 A operands,
 //      V in a swizzled unpadded LDS tile, the rows 16 at a time, so that four
 //      workgroups share a compute unit and the page loads overlap;
-//   3. merge: per (query, head), the partials of its selected slots combine in
-//      slot order (deterministic; no float atomics).
+//   3. merge: per (query, head), the partials of its selected slots, found
+//      through the map's record, combine in slot order (deterministic; no
+//      float atomics).
 #include <algorithm>
 
 #include "decode_tile.hpp"
@@ -65,8 +69,11 @@ struct PrefillWs {
     int32_t* small;      // [NB + 1]: [0] = nonempty buckets of at most kSmallRows rows, then ids
     int32_t* tile_base;  // [max_tiles, maxblk] a tile's first position within a bucket
     int32_t* entries;    // [total_q * Hkv * k]: query << 4 | slot, grouped by bucket
-    uint16_t* part_o;    // [total_q, Hq, k, 128] bf16
-    float* part_lse;     // [total_q, Hq, k]
+    int32_t* pos_of;     // [total_q, Hkv, k]: position in entries of selection (t, g, slot), -1 if none
+    uint16_t* part_o;    // [total_q * Hq * k, 128] bf16 partial outputs: row e G + n = head n of
+                         // the group for the entry at position e (inverse-map form), row
+                         // (t Hq + h) k + slot (multi-query form)
+    float* part_lse;     // [total_q * Hq * k]: their log-sum-exps, the same rows
     uint16_t* trash_o;   // [128] bf16: where padding rows' partial stores go
     float* trash_lse;    // [64]
 };
@@ -89,6 +96,8 @@ __host__ __device__ inline PrefillWs prefill_ws(void* base, int B, int Hkv, int 
     w.tile_base = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)max_tiles(total_q, B, Hkv) * maxblk * 4);
     w.entries = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)total_q * Hkv * kTopK * 4);
+    w.pos_of = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)total_q * Hkv * kTopK * 4);
     w.part_o = reinterpret_cast<uint16_t*>(p);
     p += align256((size_t)total_q * Hq * kTopK * kHeadDim * 2);
@@ -428,27 +437,33 @@ void inverse_map_small_kernel(const int32_t* __restrict__ sel, const int32_t* __
     }
     __syncthreads();
 
-    // place: entries[offset + rank] = query << 4 | slot
+    // place: entries[offset + rank] = query << 4 | slot, and the position
+    // (or -1) in pos_of
     auto off_at = [&](int i) { return (int)((cnt2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); };
 #pragma unroll
     for (int k = 0; k < kSmallSelPer; ++k) {
         const int e = tid + kSmallMapThreads * k;
         const int b = selv[k];
-        if (e < n_sel && b >= 0 && b < maxblk) {
-            const int bk = bucket_of(e, b);
-            const int t = e / (Hkv * kTopK);
-            w.entries[off_at(bk) + rank[e]] = (t << 4) | (e % kTopK);
+        if (e < n_sel) {
+            int pos = -1;
+            if (b >= 0 && b < maxblk) {
+                pos = off_at(bucket_of(e, b)) + rank[e];
+                w.entries[pos] = ((e / (Hkv * kTopK)) << 4) | (e % kTopK);
+            }
+            w.pos_of[e] = pos;
         }
     }
 }
 
 // Pass 3: the tile places each selection at offsets[bucket] + its tile's base
 // in the bucket + its rank among the tile's selections of that block (LDS
-// counters; entries within a bucket are in no particular order).
+// counters; entries within a bucket are in no particular order), and records
+// that position, or -1 for a slot that selects nothing, in pos_of.
 __global__ __launch_bounds__(kMapThreads)
 void bucket_fill_kernel(const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
                         const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_base,
-                        int32_t* __restrict__ entries, int B, int Hkv, int maxblk) {
+                        int32_t* __restrict__ entries, int32_t* __restrict__ pos_of, int B, int Hkv,
+                        int maxblk) {
     extern __shared__ int32_t cur[];  // [maxblk]
     __shared__ int sh[2];
     for (int b = threadIdx.x; b < maxblk; b += kMapThreads) cur[b] = 0;
@@ -471,9 +486,15 @@ void bucket_fill_kernel(const int32_t* __restrict__ sel, const int32_t* __restri
             base[u] = bv[u] >= 0 ? offsets[bucket0 + bv[u]] + tile_base[(size_t)blockIdx.x * maxblk + bv[u]] : 0;
 #pragma unroll
         for (int u = 0; u < kMapBatch; ++u) {
-            if (bv[u] >= 0) {
-                const int e = e0 + kMapThreads * u;
-                entries[base[u] + atomicAdd(&cur[bv[u]], 1)] = ((m.t0 + e / kTopK) << 4) | (e % kTopK);
+            const int e = e0 + kMapThreads * u;
+            if (e < n) {
+                const int t = m.t0 + e / kTopK;
+                int pos = -1;
+                if (bv[u] >= 0) {
+                    pos = base[u] + atomicAdd(&cur[bv[u]], 1);
+                    entries[pos] = (t << 4) | (e % kTopK);
+                }
+                pos_of[((size_t)t * Hkv + m.g) * kTopK + e % kTopK] = pos;
             }
         }
     }
@@ -545,14 +566,13 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     uint16_t* tbuf = tiles + wave * 32 * kKStride;  // this wave's 32-row staging tile
 
     // Row n of a tile: its (query << 4 | slot) entry -- fetched two tiles
-    // ahead -- and from it the query, head and slot.  Rows past the bucket
-    // repeat its last row (real data; results discarded).
+    // ahead -- and from it the query and head.  Rows past the bucket repeat
+    // its last row (real data; results discarded).
     auto entry_of = [&](int tile) { return w.entries[base + min(tile * 32 + n, nrows - 1) / G]; };
-    auto row_info = [&](int tile, int entry, int* t_out, int* head_out, int* slot_out) {
+    auto row_info = [&](int tile, int entry, int* t_out, int* head_out) {
         const int rho0 = tile * 32 + n;
         const int rho = rho0 < nrows ? rho0 : nrows - 1;
         *t_out = entry >> 4;
-        *slot_out = entry & 15;
         *head_out = g * G + rho % G;
         return rho0 < nrows;
     };
@@ -575,9 +595,9 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // in turn, so that while a tile computes the gathers of this wavefront's
     // next two tiles are in flight (the kernel's rate is set by the bytes it
     // keeps in flight: one workgroup per compute unit).
-    int tA = 0, hA = 0, sA = 0, tB = 0, hB = 0, sB = 0;
-    bool okA = row_info(tile, entry_of(tile), &tA, &hA, &sA);
-    bool okB = row_info(tile + kWaves, entry_of(tile + kWaves), &tB, &hB, &sB);
+    int tA = 0, hA = 0, tB = 0, hB = 0;
+    bool okA = row_info(tile, entry_of(tile), &tA, &hA);
+    bool okB = row_info(tile + kWaves, entry_of(tile + kWaves), &tB, &hB);
     int entry_next = entry_of(tile + 2 * kWaves);
     u32x4 qA[8], qB[8];
     gather_q(tA, hA, qA);
@@ -588,12 +608,12 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // unconstrained)
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    auto step = [&](u32x4 (&qraw)[8], int& t, int& head, int& slot, bool& row_ok) {
+    auto step = [&](u32x4 (&qraw)[8], int& t, int& head, bool& row_ok) {
         // B operands (k-step i of lane half h: dims 64h + 8i .. +7)
         bf16x8 qb[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) qb[i] = as_bf16x8(qraw[i]);
-        const int cur_t = t, cur_slot = slot, cur_head = head;
+        const int cur_t = t;
         const bool cur_ok = row_ok;
         // The rows two tiles ahead go into this buffer once this tile's
         // S^T products have read it (so the old and new rows never share
@@ -626,7 +646,7 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
             // keep the scheduler from hoisting further tiles' operand reads
             __builtin_amdgcn_sched_barrier(0);
         }
-        row_ok = row_info(ahead, entry_next, &t, &head, &slot);
+        row_ok = row_info(ahead, entry_next, &t, &head);
         gather_q(t, head, qraw);
         entry_next = entry_after;
 
@@ -713,18 +733,19 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                           pack2_bf16(oacc[mt][4 * qd + 2] * inv, oacc[mt][4 * qd + 3] * inv)};
             }
         __builtin_amdgcn_wave_barrier();
-        // partial row index (t * Hq + head) * k + slot < 2^31, or -1 for padding rows
-        const int orow = cur_ok ? (cur_t * Hq + cur_head) * kTopK + cur_slot : -1;
+        // partial-output row of bucket row rho = tile 32 + n: (base + rho / G)
+        // G + rho % G = base G + rho, so a tile's rows are consecutive (and
+        // stored with streaming stores); -1 for padding rows
+        const int orow = cur_ok ? base * G + tile * 32 + n : -1;
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int r = lane / 16 + 4 * it;
             const int o = __shfl(orow, r, kWave);
             const u32x4 v = *reinterpret_cast<const u32x4*>(tbuf + r * kKStride + 8 * (lane % 16));
             uint16_t* dst = (o >= 0) ? w.part_o + (size_t)o * kHeadDim : w.trash_o;
-            *reinterpret_cast<u32x4*>(dst + 8 * (lane % 16)) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 8 * (lane % 16)));
         }
-        float* ldst = (cur_ok && h == 0) ? w.part_lse + ((size_t)cur_t * Hq + cur_head) * kTopK + cur_slot
-                                         : w.trash_lse + lane;
+        float* ldst = (cur_ok && h == 0) ? w.part_lse + orow : w.trash_lse + lane;
         *ldst = mx * scale_log2 * kLn2 + __logf(sum);
         __builtin_amdgcn_wave_barrier();
         };
@@ -732,12 +753,12 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // no exit between its two steps, so that each step's wait is exact
     const int mine = (ceil_div(nrows, 32) - wave + kWaves - 1) / kWaves;  // >= 1
     for (int pair = 0; pair < mine / 2; ++pair) {
-        step(qA, tA, hA, sA, okA);
+        step(qA, tA, hA, okA);
         tile += kWaves;
-        step(qB, tB, hB, sB, okB);
+        step(qB, tB, hB, okB);
         tile += kWaves;
     }
-    if (mine & 1) step(qA, tA, hA, sA, okA);
+    if (mine & 1) step(qA, tA, hA, okA);
 }
 
 // Small buckets (at most kSmallRows (query, head) rows): one 256-thread
@@ -751,7 +772,8 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
 // A block is loaded (load_small: V rows, tokens at or past nv zero, then K
 // rows; tokens past nv are read from the page's padding and masked to -inf
 // later) and then attended (compute_small) against nrows rows: row rho is
-// head g G + rho % G of the (query << 4 | slot) entry entry_at(rho / G).
+// head g G + rho % G of the (query << 4 | slot) entry entry_at(rho / G), and
+// its partial output and log-sum-exp go to row row_of(rho).
 // Every thread of the workgroup calls both; compute_small starts by writing
 // the V tile, so a caller that attends several blocks puts a barrier between
 // calls.
@@ -771,11 +793,11 @@ __device__ __forceinline__ void load_small(const uint16_t* __restrict__ kp,
     load_k_rows(kp, tid / kWave, tid % kWave, r.k);
 }
 
-template <class EntryAt>
+template <class EntryAt, class RowOf>
 __device__ __forceinline__ void compute_small(DecodeShared& sh, const SmallRaw& r,
                                               const uint16_t* __restrict__ q, int nv, int pos0,
                                               int b, int g, int G, int Hq, int nrows,
-                                              EntryAt entry_at, const PrefillWs& w,
+                                              EntryAt entry_at, RowOf row_of, const PrefillWs& w,
                                               float scale_log2) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -793,14 +815,12 @@ __device__ __forceinline__ void compute_small(DecodeShared& sh, const SmallRaw& 
         *reinterpret_cast<u32x4*>(sh.vs + vs_off(tid / 16 + 16 * it, 8 * (tid % 16))) = r.v[it];
 
     for (int r0 = 0; r0 < nrows; r0 += 16) {
-        // row n of this group: its query, head and slot (rows past the bucket
+        // row n of this group: its query and head (rows past the bucket
         // repeat its last row; their results are discarded)
         const int rho0 = r0 + n;
         const bool row_ok = rho0 < nrows;
         const int rho = row_ok ? rho0 : nrows - 1;
-        const int entry = entry_at(rho / G);
-        const int t = entry >> 4;
-        const int slot = entry & 15;
+        const int t = entry_at(rho / G) >> 4;
         const int head = g * G + rho % G;
         bf16x8 qb[4];
         const uint16_t* qrow = q + ((size_t)t * Hq + head) * kHeadDim;
@@ -870,7 +890,7 @@ __device__ __forceinline__ void compute_small(DecodeShared& sh, const SmallRaw& 
         }
         const float l = sh.red_sum[0][n] + sh.red_sum[1][n] + sh.red_sum[2][n] + sh.red_sum[3][n];
         if (row_ok) {
-            const size_t prow = ((size_t)t * Hq + head) * kTopK + slot;
+            const size_t prow = row_of(rho);
             const float inv = 1.0f / l;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
@@ -910,7 +930,8 @@ void bucket_small_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     SmallRaw raw;
     load_small(k_cache + page_off, v_cache + page_off, nv, raw);
     compute_small(sh, raw, q, nv, pos0, b, g, G, Hq, cnt * G,
-                  [&](int i) { return w.entries[base + i]; }, w, scale_log2);
+                  [&](int i) { return w.entries[base + i]; },
+                  [&](int rho) { return (size_t)base * G + rho; }, w, scale_log2);
 }
 
 // Few queries per sequence (multi-query decode: a handful of draft tokens
@@ -1083,10 +1104,16 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
             if (eb[i] == b) rows[at++] = (uint16_t)(tid + kDecThreads * i);
         n_rows_b = __builtin_amdgcn_readfirstlane(n_rows_b);
         __syncthreads();  // rows visible
+        // partials at row (t, head, slot): this form has no entry list, and
+        // its merge reads them there
         compute_small(sh, r, q, nv_of(b), pos0, b, g, G, Hq, n_rows_b * G,
                       [&](int i) {
                           const int e = rows[i];
                           return ((t0 + e / kTopK) << 4) | (e % kTopK);
+                      },
+                      [&](int rho) {
+                          const int e = rows[rho / G];
+                          return ((size_t)(t0 + e / kTopK) * Hq + g * G + rho % G) * kTopK + e % kTopK;
                       },
                       w, scale_log2);
     };
@@ -1097,7 +1124,11 @@ void mq_block_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     }
 }
 
-// 16 threads per (query, head), 8 dims each: merge the selected slots' partials.
+// 16 threads per (query, head), 8 dims each: merge the selected slots'
+// partials.  Slot i's partial is at row pos_of[(t Hkv + g) k + i] G + n
+// (pos_of -1: no selection), or, with DIRECT (the multi-query form, which
+// has no entry list), at row (t Hq + h) k + i when sel names a block there.
+template <bool DIRECT>
 __global__ __launch_bounds__(256)
 void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
                           uint16_t* __restrict__ out, float* __restrict__ lse_out, int total_q,
@@ -1108,24 +1139,31 @@ void prefill_merge_kernel(const int32_t* __restrict__ sel, PrefillWs w,
     if (th >= total_q * Hq) return;
     const int t = th / Hq;
     const int hh = th % Hq;
-    const int g = hh / (Hq / Hkv);
-    const int32_t* srow = sel + ((size_t)t * Hkv + g) * kTopK;
-    const float* lp = w.part_lse + (size_t)th * kTopK;
-    // every slot's partial is loaded together with the selection (a slot that
-    // is not a selection -- index outside [0, maxblk) -- holds stale workspace
-    // values and is dropped by selects, never by a multiply)
+    const int G = Hq / Hkv;
+    const size_t tg = ((size_t)t * Hkv + hh / G) * kTopK;
+    // each slot's row, then every partial loaded together (a slot with no
+    // selection reads a row of its own and is dropped by selects, never by a
+    // multiply, so a stale non-finite value cannot leak in)
     bool ok[kTopK];
+    size_t row[kTopK];
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) {
+        if (DIRECT) {
+            const int b = sel[tg + i];
+            ok[i] = b >= 0 && b < maxblk;
+            row[i] = (size_t)th * kTopK + i;
+        } else {
+            const int pe = w.pos_of[tg + i];
+            ok[i] = pe >= 0;
+            row[i] = (size_t)(ok[i] ? pe : 0) * G + hh % G;
+        }
+    }
     float li[kTopK];
     u32x4 oi[kTopK];
 #pragma unroll
     for (int i = 0; i < kTopK; ++i) {
-        li[i] = lp[i];
-        oi[i] = ld16_stream(w.part_o + ((size_t)th * kTopK + i) * kHeadDim + 8 * part);
-    }
-#pragma unroll
-    for (int i = 0; i < kTopK; ++i) {
-        const int b = srow[i];
-        ok[i] = b >= 0 && b < maxblk;
+        li[i] = w.part_lse[row[i]];
+        oi[i] = ld16_stream(w.part_o + row[i] * kHeadDim + 8 * part);
     }
     float mx = -__builtin_inff();
 #pragma unroll
@@ -1195,7 +1233,7 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                                dim3(kDecThreads), 0, st, q, k_cache, v_cache, block_table, seq_lens,
                                cu_q, sel_rw, nullptr, w, s.Hq, s.Hkv, s.maxblk, P, s.scale * kLog2e);
         const int nth = total_q * s.Hq * 16;
-        hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel,
+        hipLaunchKernelGGL(prefill_merge_kernel<true>, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel,
                            w, out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
         return hipGetLastError();
     }
@@ -1210,7 +1248,7 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets,
                            w.buckets, w.small, NB, small_cnt);
         hipLaunchKernelGGL(bucket_fill_kernel, dim3(tiles), dim3(kMapThreads), map_lds, st, sel,
-                           cu_q, w.offsets, w.tile_base, w.entries, s.B, s.Hkv, s.maxblk);
+                           cu_q, w.offsets, w.tile_base, w.entries, w.pos_of, s.B, s.Hkv, s.maxblk);
     }
     // at most one nonempty bucket per selection, and at most one bucket of
     // more than small_cnt entries per small_cnt + 1 selections
@@ -1225,7 +1263,7 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
                        v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
     const int nth = total_q * s.Hq * 16;
-    hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
+    hipLaunchKernelGGL(prefill_merge_kernel<false>, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
                        out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
     return hipGetLastError();
 }
@@ -1286,7 +1324,7 @@ hipError_t msa_launch_multi_query_step(const MsaShape& s, int total_q, const uin
     }
 #undef MSA_MQ
     const int nth = total_q * s.Hq * 16;
-    hipLaunchKernelGGL(prefill_merge_kernel, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
+    hipLaunchKernelGGL(prefill_merge_kernel<true>, dim3(ceil_div(nth, 256)), dim3(256), 0, st, sel, w,
                        out, lse, total_q, s.Hq, s.Hkv, s.maxblk);
     return hipGetLastError();
 }
