@@ -553,9 +553,10 @@ def record_traffic(name, copy_f, copy_w, fetch, write):
 
 def measured_ceilings(chain=None):
     """Sustained HBM read bandwidth and bf16 matrix-core rate on this GPU, from
-    the separate calibration library: the best over a few grid sizes of a
-    2 GiB streaming read; the same for 64 MiB reads (the size of one decode
-    layer-step's two passes) cycling over 32 distinct slices; and independent
+    the separate calibration library: the best over grid-stride and
+    chunk-per-workgroup forms of a 2 GiB streaming read; the same for 64 MiB
+    reads (the size of one decode layer-step's two passes) cycling over 32
+    distinct slices; device copies of 800 and 96 MiB; and independent
     32x32x16 products at 4 and 8 waves per SIMD.  With chain = (a, b, c)
     bytes, also the time of three dependent contiguous reads of a, b and c
     bytes, one launch each, back to back over distinct slices: the floor of
@@ -571,6 +572,10 @@ def measured_ceilings(chain=None):
     c.msa_calib_read_sink_len.restype = ctypes.c_size_t
     c.msa_calib_copy_grid.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_int, ctypes.c_void_p]
+    c.msa_calib_read_chunked.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    c.msa_calib_copy_chunked.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_size_t, ctypes.c_void_p]
     c.msa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     c.msa_calib_mfma_flop.restype = ctypes.c_double
     c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -582,9 +587,30 @@ def measured_ceilings(chain=None):
     iters = 16384
     out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
 
-    def read(ptr, size, grid):
-        if c.msa_calib_read_grid(ptr, size, grid, sink.data_ptr(), sink.numel(), st) != 0:
-            raise RuntimeError("msa_calib_read_grid failed")
+    # two forms of each: grid-stride loops over a fixed grid ("grid", workgroups)
+    # and one short-lived workgroup per contiguous chunk ("chunk", KiB)
+    forms = [("grid", g) for g in (256, 512, 1024, 4096)] + [("chunk", k) for k in (16, 32, 64)]
+
+    def read(ptr, size, form):
+        kind, v = form
+        if kind == "grid":
+            rc = c.msa_calib_read_grid(ptr, size, v, sink.data_ptr(), sink.numel(), st)
+        else:
+            rc = c.msa_calib_read_chunked(ptr, size, v << 10, sink.data_ptr(), sink.numel(), st)
+        if rc != 0:
+            raise RuntimeError("msa_calib_read failed")
+
+    def copy_bytes(src, dst, size, form):
+        kind, v = form
+        if kind == "grid":
+            rc = c.msa_calib_copy_grid(src, dst, size, v, st)
+        else:
+            rc = c.msa_calib_copy_chunked(src, dst, size, v << 10, st)
+        if rc != 0:
+            raise RuntimeError("msa_calib_copy failed")
+
+    def name(form):
+        return f"{form[1]} workgroups grid-stride" if form[0] == "grid" else f"{form[1]} KiB per workgroup"
 
     def mfma(blocks):
         if c.msa_calib_mfma(out.data_ptr(), blocks, iters, st) != 0:
@@ -592,43 +618,39 @@ def measured_ceilings(chain=None):
 
     big, sized = {}, {}
     base = buf.data_ptr()
-    for grid in (256, 512, 1024, 4096):
-        ms = time_calls([lambda g=grid: read(base, nbytes, g)], 6, 2)
-        big[grid] = nbytes / (ms * 1e-3) / 1e9
-        fns = [lambda i=i, g=grid: read(base + i * small, small, g) for i in range(nbytes // small)]
+    for form in forms:
+        ms = time_calls([lambda f=form: read(base, nbytes, f)], 6, 2)
+        big[form] = nbytes / (ms * 1e-3) / 1e9
+        fns = [lambda i=i, f=form: read(base + i * small, small, f) for i in range(nbytes // small)]
         ms = time_calls(fns, 2 * len(fns), len(fns))
-        sized[grid] = small / (ms * 1e-3) / 1e9
+        sized[form] = small / (ms * 1e-3) / 1e9
     # a device copy of 800 MiB (1.6 GiB of traffic, half reads and half
     # writes: the mix and size of the prefill block-major kernel's traffic)
     half = 800 << 20
     copy = {}
-    for grid in (1024, 2048, 4096):
-        def cp(g=grid):
-            if c.msa_calib_copy_grid(base, base + half, half, g, st) != 0:
-                raise RuntimeError("msa_calib_copy_grid failed")
-        ms = time_calls([cp], 6, 2)
-        copy[grid] = 2 * half / (ms * 1e-3) / 1e9
+    for form in forms:
+        ms = time_calls([lambda f=form: copy_bytes(base, base + half, half, f)], 6, 2)
+        copy[form] = 2 * half / (ms * 1e-3) / 1e9
     # the same copy of 96 MiB each way, a footprint the 256 MB Infinity Cache
     # holds: what keeping a round trip's data in that cache could gain
     small_half = 96 << 20
     copy_small = {}
-    for grid in (1024, 2048, 4096):
-        def cps(g=grid):
-            if c.msa_calib_copy_grid(base, base + small_half, small_half, g, st) != 0:
-                raise RuntimeError("msa_calib_copy_grid failed")
-        ms = time_calls([cps], 40, 8)
-        copy_small[grid] = 2 * small_half / (ms * 1e-3) / 1e9
+    for form in forms:
+        ms = time_calls([lambda f=form: copy_bytes(base, base + small_half, small_half, f)], 40, 8)
+        copy_small[form] = 2 * small_half / (ms * 1e-3) / 1e9
     chain_us = None
     if chain:
+        # each read in the form fastest at 64 MiB, or one 16 KiB chunk per
+        # workgroup for the small one
         sizes = [int(n) // 16 * 16 for n in chain]
         span = sum(sizes)
-        grids = [max(sized, key=sized.get) if n > small // 4 else min(4096, -(-n // (16 * 256)))
-                 for n in sizes]
+        best_small = max(sized, key=sized.get)
+        kinds = [best_small if n > small // 4 else ("chunk", 16) for n in sizes]
 
         def chain_call(i):
             off = base + i * span
-            for n, g in zip(sizes, grids):
-                read(off, n, g)
+            for n, f in zip(sizes, kinds):
+                read(off, n, f)
                 off += n
         fns = [lambda i=i: chain_call(i) for i in range(nbytes // span)]
         chain_us = time_calls(fns, 4 * len(fns), len(fns)) * 1e3
@@ -645,20 +667,23 @@ def measured_ceilings(chain=None):
     gc = max(copy, key=copy.get)
     gcs = max(copy_small, key=copy_small.get)
     res = {"hbm_read_gbs": round(big[gb], 1),
-            "hbm_read_64mib_gbs": round(sized[gs], 1),
-            "hbm_copy_800mib_gbs": round(copy[gc], 1),
-            "copy_96mib_gbs": round(copy_small[gcs], 1),
-            "mfma_bf16_tflops": round(tflops[bm], 1),
-            "vendor_gemm_bf16_randn_tflops": round(vendor["randn"], 1),
-            "vendor_gemm_bf16_const_tflops": round(vendor["const"], 1),
-            "gpu_max_clock_mhz": clock,
-            "how": f"non-temporal streaming read of 2 GiB (best grid {gb} workgroups of 256) "
-                   f"and of 64 MiB slices back to back (best grid {gs}); a device copy of 800 MiB "
-                   f"(read + write bytes, best grid {gc}) and of 96 MiB (best grid {gcs}); 32x32x16 bf16 MFMA "
-                   f"loop on constant operands, 4 independent chains per wave, {bm // 256 * 4} waves "
-                   f"per CU; torch.matmul (hipBLASLt) bf16 8192^3 on N(0,1) and on all-ones operands",
-            "read_gbs_by_grid": {str(k): round(v, 1) for k, v in big.items()},
-            "read_64mib_gbs_by_grid": {str(k): round(v, 1) for k, v in sized.items()}}
+           "hbm_read_64mib_gbs": round(sized[gs], 1),
+           "hbm_copy_800mib_gbs": round(copy[gc], 1),
+           "copy_96mib_gbs": round(copy_small[gcs], 1),
+           "mfma_bf16_tflops": round(tflops[bm], 1),
+           "vendor_gemm_bf16_randn_tflops": round(vendor["randn"], 1),
+           "vendor_gemm_bf16_const_tflops": round(vendor["const"], 1),
+           "gpu_max_clock_mhz": clock,
+           "how": f"non-temporal streaming read of 2 GiB (best: {name(gb)}) "
+                  f"and of 64 MiB slices back to back (best: {name(gs)}); a device copy of 800 MiB "
+                  f"(read + write bytes, best: {name(gc)}) and of 96 MiB (best: {name(gcs)}), "
+                  f"each the fastest of grid-stride loops over 256-4096 workgroups of 256 threads "
+                  f"and one workgroup per 16, 32 or 64 KiB chunk; 32x32x16 bf16 MFMA "
+                  f"loop on constant operands, 4 independent chains per wave, {bm // 256 * 4} waves "
+                  f"per CU; torch.matmul (hipBLASLt) bf16 8192^3 on N(0,1) and on all-ones operands",
+           "read_gbs_by_form": {name(k): round(v, 1) for k, v in big.items()},
+           "read_64mib_gbs_by_form": {name(k): round(v, 1) for k, v in sized.items()},
+           "copy_800mib_gbs_by_form": {name(k): round(v, 1) for k, v in copy.items()}}
     if chain_us is not None:
         res["three_read_launches_us"] = round(chain_us, 2)
         res["three_read_launches_bytes"] = [int(n) for n in chain]

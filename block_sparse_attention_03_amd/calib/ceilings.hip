@@ -1,6 +1,6 @@
 // ceilings.hip -- measured ceilings for the roofline fractions: a streaming
 // HBM read, a device copy (reads and writes at once) and a bf16 matrix-core
-// loop on MI355X (gfx950).  Not part of the
+// loop on MI355X (gfx950), each in the forms that probes found fastest.  Not part of the
 // MSA library: the benchmark loads this separate libmsa_calib.so to report
 // achieved bandwidth and FLOP rate against what the chip actually sustains,
 // next to the published peaks.
@@ -16,9 +16,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
+// The sink store depends on every load, so none can be dropped; it runs only
+// if the XOR of a thread's words equals this value, which never happens for
+// the zero-filled buffers the benchmark reads, so the reads are the only
+// traffic.
+constexpr uint32_t kNever = 0x12345678u;
+
 // Every 16-byte chunk of buf read once with streaming (non-temporal) loads,
-// eight in flight per thread; one word per thread goes to sink so the loads
-// cannot be dropped.
+// eight in flight per thread, grid-stride.
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ buf, size_t n16,
                                                         uint32_t* __restrict__ sink) {
     const size_t stride = (size_t)gridDim.x * kThreads;
@@ -35,7 +40,48 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
         const u32x4 v = __builtin_nontemporal_load(buf + i);
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
-    sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+    if (acc == kNever) sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+// Workgroup b reads the chunk [b chunk, (b + 1) chunk) of 16-byte units, four
+// loads in flight per thread: many short-lived workgroups, the form that
+// streams fastest on this chip.
+__global__ __launch_bounds__(kThreads) void read_chunk_kernel(const u32x4* __restrict__ buf,
+                                                              size_t n16, size_t chunk,
+                                                              uint32_t* __restrict__ sink) {
+    const size_t b0 = (size_t)blockIdx.x * chunk;
+    const size_t b1 = b0 + chunk < n16 ? b0 + chunk : n16;
+    size_t i = b0 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < b1; i += kThreads) {
+        const u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == kNever) sink[threadIdx.x] = acc;
+}
+
+// dst = src by chunks as read_chunk_kernel reads, with streaming stores.
+__global__ __launch_bounds__(kThreads) void copy_chunk_kernel(const u32x4* __restrict__ src,
+                                                              u32x4* __restrict__ dst, size_t n16,
+                                                              size_t chunk) {
+    const size_t b0 = (size_t)blockIdx.x * chunk;
+    const size_t b1 = b0 + chunk < n16 ? b0 + chunk : n16;
+    size_t i = b0 + threadIdx.x;
+    for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], dst + i + u * kThreads);
+    }
+    for (; i < b1; i += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // dst = src, 16-byte chunks with streaming loads, eight in flight per thread:
@@ -119,6 +165,42 @@ int msa_calib_copy_grid(const void* src, void* dst, size_t bytes, int blocks, vo
     hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                        static_cast<u32x4*>(dst), bytes / 16);
+    return (int)hipGetLastError();
+}
+
+// Streams `bytes` (a multiple of 16) at buf, one workgroup per `chunk_bytes`
+// (a multiple of 16, at least 4096) of it.
+int msa_calib_read_chunked(const void* buf, size_t bytes, size_t chunk_bytes, uint32_t* sink,
+                           size_t sink_len, void* stream) {
+    if (!buf || !sink || bytes % 16 != 0 || chunk_bytes % 16 != 0 || chunk_bytes < 4096 ||
+        sink_len < (size_t)kThreads)
+        return (int)hipErrorInvalidValue;
+    const size_t chunk = chunk_bytes / 16;
+    const size_t grid = (bytes / 16 + chunk - 1) / chunk;
+    if (grid == 0) return 0;
+    if (grid > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_chunk_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), bytes / 16,
+                       chunk, sink);
+    return (int)hipGetLastError();
+}
+
+// Copies `bytes` from src to dst (not overlapping), one workgroup per
+// `chunk_bytes` (as msa_calib_read_chunked).
+int msa_calib_copy_chunked(const void* src, void* dst, size_t bytes, size_t chunk_bytes,
+                           void* stream) {
+    if (!src || !dst || bytes % 16 != 0 || chunk_bytes % 16 != 0 || chunk_bytes < 4096)
+        return (int)hipErrorInvalidValue;
+    const char* a = static_cast<const char*>(src);
+    const char* b = static_cast<const char*>(dst);
+    if (a < b + bytes && b < a + bytes) return (int)hipErrorInvalidValue;
+    const size_t chunk = chunk_bytes / 16;
+    const size_t grid = (bytes / 16 + chunk - 1) / chunk;
+    if (grid == 0) return 0;
+    if (grid > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), bytes / 16, chunk);
     return (int)hipGetLastError();
 }
 

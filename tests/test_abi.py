@@ -187,8 +187,8 @@ def test_calibration_library_exports():
     path = os.path.join(os.path.dirname(L.LIB_PATH), "libmsa_calib.so")
     c = ctypes.CDLL(path)
     for name in ("msa_calib_read_blocks", "msa_calib_read_sink_len", "msa_calib_read",
-                 "msa_calib_read_grid", "msa_calib_copy_grid", "msa_calib_mfma_flop",
-                 "msa_calib_mfma"):
+                 "msa_calib_read_grid", "msa_calib_copy_grid", "msa_calib_read_chunked",
+                 "msa_calib_copy_chunked", "msa_calib_mfma_flop", "msa_calib_mfma"):
         assert hasattr(c, name), name
     c.msa_calib_mfma_flop.restype = ctypes.c_double
     c.msa_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
@@ -201,6 +201,15 @@ def test_calibration_library_exports():
                                       ctypes.c_int, ctypes.c_void_p]
     assert c.msa_calib_copy_grid(None, P(0x1000), 16, 4, None) != 0
     assert c.msa_calib_copy_grid(P(0x1000), P(0x1010), 32, 4, None) != 0  # overlapping
+    c.msa_calib_read_chunked.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_size_t,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert c.msa_calib_read_chunked(None, 16, 4096, P(0x1000), 256, None) != 0
+    assert c.msa_calib_read_chunked(P(0x1000), 16, 1024, P(0x1000), 256, None) != 0  # chunk too small
+    assert c.msa_calib_read_chunked(P(0x1000), 16, 4096, P(0x1000), 255, None) != 0  # sink too short
+    c.msa_calib_copy_chunked.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+    assert c.msa_calib_copy_chunked(P(0x1000), P(0x1010), 32, 4096, None) != 0  # overlapping
+    assert c.msa_calib_copy_chunked(P(0x1000), P(0x100000), 24, 4096, None) != 0  # not 16-byte
 
 
 def test_validate_inputs_errors():
