@@ -257,6 +257,11 @@ __device__ __forceinline__ int wave_candidates(int b_loc, int w) {
 template <int NPT, int W, class Out>
 __device__ void select_row(const float (&raw)[NPT], const int (&page)[NPT], int b_loc, int w,
                            int lane, SelectShared<W>* sh, Out&& out) {
+    // b_loc and w are the same on every lane of the wavefront; saying so keeps
+    // the counts, kk and the thresholds in scalar registers, so the searches
+    // below run as scalar loops instead of exec-masked vector code
+    b_loc = __builtin_amdgcn_readfirstlane(b_loc);
+    w = __builtin_amdgcn_readfirstlane(w);
     const int base = w * NPT * kWave;
     uint32_t key[NPT];
 #pragma unroll
