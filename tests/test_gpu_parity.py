@@ -96,6 +96,48 @@ def test_random_shapes_against_the_oracle(seed):
         assert torch.equal(fused.lse, step.lse)
 
 
+def _random_large_config(seed: int) -> "gen.MsaConfig":
+    """Larger seeded shapes: 1-8 sequences of 200 to 140,000 tokens
+    (log-uniform), H_kv in {1, 2, 4, 8}, G in {1, 2, 4, 6, 8}; one new token
+    per sequence, a few drafts, or up to 2,048 new tokens per sequence."""
+    rng = np.random.default_rng(7000 + seed)
+    b = int(rng.integers(1, 9))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 6, 8]))
+    lens = [int(np.exp(rng.uniform(np.log(200), np.log(140000)))) for _ in range(b)]
+    mode = seed % 3
+    if mode == 0:
+        n_new = [1] * b
+    elif mode == 1:
+        n_new = [int(rng.integers(1, 9)) for _ in range(b)]
+    else:
+        n_new = [int(rng.integers(0, min(L, 2048) + 1)) for L in lens]
+    n_new = [min(n, L) for n, L in zip(n_new, lens)]
+    if sum(n_new) == 0:
+        n_new[0] = 1
+    hidx = hkv if rng.integers(0, 3) == 0 else 1
+    return gen.MsaConfig(f"random_large_{seed}", lens, n_new, g * hkv, hkv, num_idx_heads=hidx,
+                         permute_pages=True, extra_pages=int(rng.integers(0, 4)), seed=3000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_large_shapes_against_the_oracle(seed):
+    """Seeded larger shapes (see _random_large_config), poisoned padding:
+    sampled scores and attention rows and every selection row against the
+    oracle; the one-call form (msa_decode_step for decode, else
+    msa_multi_query_step) bit-equal to the separate calls."""
+    cfg = _random_large_config(seed)
+    print(f"[random] {cfg.name}: lens={cfg.seq_lens} n_new={cfg.n_new} "
+          f"Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} Hidx={cfg.num_idx_heads}", flush=True)
+    x, step = parity.full_check(cfg, poison=True, score_rows=2048, attn_rows=1024)
+    one = MsaStep(x, fused=True) if cfg.is_decode else MsaStep(x, multi=True)
+    one.run()
+    torch.cuda.synchronize()
+    assert torch.equal(one.sel, step.sel)
+    assert torch.equal(one.out, step.out)
+    assert torch.equal(one.lse, step.lse)
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_cases_poisoned_padding(cfg):
     parity.full_check(cfg, poison=True)
