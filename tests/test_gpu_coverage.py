@@ -74,13 +74,16 @@ def test_selection_width_bands(cfg):
     assert torch.equal(fused.lse, step.lse)
 
 
-def test_prefill_row_with_no_selection():
+@pytest.mark.parametrize("n_new", [[130, 40], [3, 2]], ids=["inverse_map", "multi_query_form"])
+def test_prefill_row_with_no_selection(n_new):
     """A (query, group) row of sel that is all -1 attends no token: its heads
     get out = 0 and lse = -inf, as the oracle defines the empty token set;
-    the other rows are unchanged and match the oracle."""
+    the other rows are unchanged and match the oracle.  Both forms of the
+    prefill entry point: the inverse map (170 queries) and the few-query
+    kernel (5 queries)."""
     import oracle
-    cfg = gen.MsaConfig("prefill_empty_rows", [2600, 900], [130, 40], 12, 3, permute_pages=True,
-                        seed=87)
+    cfg = gen.MsaConfig(f"prefill_empty_rows_{sum(n_new)}", [2600, 900], n_new, 12, 3,
+                        permute_pages=True, seed=87)
     print(f"[empty-row] {cfg.name}", flush=True)
     x = gen.make_inputs(cfg, device="cuda", poison_padding=True)
     step = MsaStep(x)
@@ -88,7 +91,7 @@ def test_prefill_row_with_no_selection():
     step.topk()
     torch.cuda.synchronize()
     T, H, G = cfg.total_q, cfg.num_kv_heads, cfg.num_q_heads // cfg.num_kv_heads
-    empty = [(0, 0), (5, 2), (129, 1), (T - 1, 0), (T - 1, 2)]
+    empty = sorted({(0, 0), (min(5, T - 1), 2), (min(129, T - 1), 1), (T - 1, 0), (T - 1, 2)})
     for t, g in empty:
         step.sel[t, g, :] = -1
     step.attend()
