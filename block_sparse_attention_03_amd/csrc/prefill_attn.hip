@@ -13,7 +13,8 @@
 //      selection, exclusive scan (which also lists the nonempty buckets),
 //      placement of (query, slot) entries;
 //   2. block-major attention: one workgroup per nonempty bucket stages the block's K
-//      and V (row-major, coalesced loads) in LDS once, then its wavefronts sweep
+//      and V (direct-to-LDS loads, 16-byte chunks swizzled by token) in LDS
+//      once, two workgroups to a compute unit, then its wavefronts sweep
 //      the bucket's (query, head) rows 32 at a time with 32x32x16 bf16 matrix
 //      cores: S^T = K Q^T, row softmax in registers, P rounded to bf16 and
 //      fed straight from the S^T accumulators as the B operand of
@@ -41,11 +42,6 @@
 namespace msa {
 namespace {
 
-constexpr int kPfThreads = 512;
-constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-byte reads of 8
-                                         // consecutive rows hit distinct banks)
-constexpr int kVStride = kHeadDim + 32;  // bf16 per V row in LDS (320 B: the transpose reads
-                                         // of 4 consecutive rows x 64 B hit distinct banks)
 // Buckets of at most this many (query, head) rows take the small-bucket kernel.
 constexpr int kSmallRows = 32;
 
@@ -500,7 +496,16 @@ void bucket_fill_kernel(const int32_t* __restrict__ sel, const int32_t* __restri
     }
 }
 
-__global__ __launch_bounds__(kPfThreads, 1)
+// Block-major attention: 256-thread workgroups that fit two to a compute
+// unit (K and V unpadded in LDS with swizzled 16-byte chunks, 64 KB, plus a
+// 16 KB output staging tile), so that one workgroup's block staging and last
+// tiles overlap the other's products.
+constexpr int kPfThreads = 256;
+__device__ __forceinline__ int bk_off(int t, int d) {  // bf16 offset of K (token t, dim d)
+    return t * kHeadDim + ((((d >> 3) ^ (t & 15))) << 3) + (d & 7);
+}
+
+__global__ __launch_bounds__(kPfThreads, 2)
 void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                         const uint16_t* __restrict__ k_cache,  // [P, Hkv, 128, 128]
                         const uint16_t* __restrict__ v_cache,
@@ -508,11 +513,11 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
                         const int32_t* __restrict__ seq_lens,
                         const int32_t* __restrict__ cu_q, PrefillWs w, int Hq, int Hkv,
                         int maxblk, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kBlock * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kVStride];
-    // per-wave staging of 32 partial-output rows: accumulator fragments in,
-    // whole 256-byte rows out as 16-byte stores
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[(kPfThreads / kWave) * 32 * kKStride];
+    // K and V unpadded (32 KB each), 16-byte chunks swizzled by token (K:
+    // bk_off, V: vs_off); per wavefront a 32-row x 64-dim output staging tile
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kBlock * kHeadDim];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kHeadDim];
+    __shared__ __attribute__((aligned(16))) uint16_t stg[(kPfThreads / kWave) * 32 * 64];
 
     if ((int)blockIdx.x >= w.buckets[0]) return;  // uniform
     const int bk = w.buckets[1 + blockIdx.x];
@@ -532,28 +537,37 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const uint16_t* vp = v_cache + page_off;
     const int tid = threadIdx.x;
 
-    // Stage the block once, K and V both row-major with coalesced 16-byte
-    // loads; tokens past the sequence end are zero.
+    // Stage the block once with direct-to-LDS loads: wavefront w's eight
+    // loads of each fill 16-byte chunks 512w .. 512w + 511 (tokens 32w ..
+    // 32w + 31); lane l of load j fills chunk position l % 16 of token
+    // (512w + 64j + l) / 16 and so reads that token's global chunk
+    // (l % 16) ^ swizzle.  The page is allocated in full; V rows past the
+    // sequence end are zeroed after the loads (P is 0 there, and 0 x a
+    // non-finite value must not reach the sum), K rows there are cut by the
+    // causal mask.
     {
-        constexpr int kIt = kBlock * kHeadDim / 8 / kPfThreads;
-        u32x4 kv[kIt], vv[kIt];
+        const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+        const int ln = tid % kWave;
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int c = tid + kPfThreads * it;
-            const int tok = c / 16, d0 = (c % 16) * 8;
-            kv[it] = (tok < nv) ? ld16_stream(kp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
-            vv[it] = (tok < nv) ? ld16_stream(vp + tok * kHeadDim + d0) : u32x4{0u, 0u, 0u, 0u};
+        for (int jl = 0; jl < 8; ++jl) {
+            const int chunk0 = (wv * 8 + jl) * kWave;
+            const int tok = (chunk0 + ln) / 16, pos = ln % 16;
+            __builtin_amdgcn_global_load_lds(kp + tok * kHeadDim + 8 * (pos ^ (tok & 15)),
+                                             (__attribute__((address_space(3))) void*)(ks + chunk0 * 8),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vp + tok * kHeadDim + 8 * (pos ^ ((tok & 7) << 1)),
+                                             (__attribute__((address_space(3))) void*)(vs + chunk0 * 8),
+                                             16, 0, 0);
         }
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int c = tid + kPfThreads * it;
-            const int tok = c / 16, d0 = (c % 16) * 8;
-            *reinterpret_cast<u32x4*>(ks + tok * kKStride + d0) = kv[it];
-            *reinterpret_cast<u32x4*>(vs + tok * kVStride + d0) = vv[it];
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wavefront's chunks are in LDS
+        __syncthreads();
+        if (nv < kBlock) {  // uniform: the sequence's partial last block
+            for (int c = tid; c < (kBlock - nv) * (kHeadDim / 8); c += kPfThreads)
+                *reinterpret_cast<u32x4*>(vs + (nv + c / 16) * kHeadDim + 8 * (c % 16)) =
+                    u32x4{0u, 0u, 0u, 0u};
+            __syncthreads();
         }
     }
-    __syncthreads();
-
     // wave-uniform to the compiler too, so the tile loop's exits are scalar
     // branches and its load waits stay exact across iterations
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -563,7 +577,6 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     const int nrows = cnt * G;
     const int tok0 = b * kBlock;
     constexpr int kWaves = kPfThreads / kWave;
-    uint16_t* tbuf = tiles + wave * 32 * kKStride;  // this wave's 32-row staging tile
 
     // Row n of a tile: its (query << 4 | slot) entry -- fetched two tiles
     // ahead -- and from it the query and head.  Rows past the bucket repeat
@@ -594,7 +607,7 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     // Query rows are gathered two tiles ahead into two register buffers used
     // in turn, so that while a tile computes the gathers of this wavefront's
     // next two tiles are in flight (the kernel's rate is set by the bytes it
-    // keeps in flight: one workgroup per compute unit).
+    // keeps in flight).
     int tA = 0, hA = 0, tB = 0, hB = 0;
     bool okA = row_info(tile, entry_of(tile), &tA, &hA);
     bool okB = row_info(tile + kWaves, entry_of(tile + kWaves), &tB, &hB);
@@ -628,17 +641,15 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         // mt+1 are read while tile mt multiplies.
         f32x16 sacc[4];
         u32x4 ka[2][8];
-        {
-            const uint16_t* krow = ks + n * kKStride + 64 * h;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ka[0][i] = *reinterpret_cast<const u32x4*>(krow + 8 * i);
-        }
+        for (int i = 0; i < 8; ++i) ka[0][i] = *reinterpret_cast<const u32x4*>(ks + bk_off(n, 64 * h + 8 * i));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (mt < 3) {
-                const uint16_t* krow = ks + (32 * (mt + 1) + n) * kKStride + 64 * h;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ka[(mt + 1) & 1][i] = *reinterpret_cast<const u32x4*>(krow + 8 * i);
+                for (int i = 0; i < 8; ++i)
+                    ka[(mt + 1) & 1][i] =
+                        *reinterpret_cast<const u32x4*>(ks + bk_off(32 * (mt + 1) + n, 64 * h + 8 * i));
             }
             sacc[mt] = mfma32(as_bf16x8(ka[mt & 1][0]), qb[0], f32x16{});
 #pragma unroll
@@ -694,20 +705,21 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         // 16*((lane/16)%2) .. +15); dim tile mt+1 is read while mt multiplies.
         f32x16 oacc[4];
         const int j = lane % 16;
-        const uint16_t* vsrc = vs + (4 * h + j / 4) * kVStride + 16 * ((lane / 16) % 2) + 4 * (j % 4);
+        const int vt = 4 * h + j / 4;
+        const int vd = 16 * ((lane / 16) % 2) + 4 * (j % 4);
         u32x2 va[2][16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            va[0][2 * i] = lds_read_tr16(vsrc + 16 * i * kVStride);
-            va[0][2 * i + 1] = lds_read_tr16(vsrc + (16 * i + 8) * kVStride);
+            va[0][2 * i] = lds_read_tr16(vs + vs_off(16 * i + vt, vd));
+            va[0][2 * i + 1] = lds_read_tr16(vs + vs_off(16 * i + 8 + vt, vd));
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (mt < 3) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    va[(mt + 1) & 1][2 * i] = lds_read_tr16(vsrc + 16 * i * kVStride + 32 * (mt + 1));
-                    va[(mt + 1) & 1][2 * i + 1] = lds_read_tr16(vsrc + (16 * i + 8) * kVStride + 32 * (mt + 1));
+                    va[(mt + 1) & 1][2 * i] = lds_read_tr16(vs + vs_off(16 * i + vt, 32 * (mt + 1) + vd));
+                    va[(mt + 1) & 1][2 * i + 1] = lds_read_tr16(vs + vs_off(16 * i + 8 + vt, 32 * (mt + 1) + vd));
                 }
             }
             const u32x2* a = va[mt & 1];
@@ -720,30 +732,40 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
         }
         sum += __shfl_xor(sum, 32, kWave);
 
-        // normalised partial output: O^T fragments -> staging tile (row n) ->
-        // coalesced 16-byte stores of 4 rows x 256 bytes per instruction
+        // normalised partial output.  Row rho = tile 32 + n of the bucket is
+        // partial row (base + rho / G) G + rho % G = base G + rho, so a tile's
+        // 32 rows are consecutive; padding rows write a trash row (-1).  Each
+        // half row (dims 64hf .. 64hf + 63) goes accumulators -> this wave's
+        // staging tile (lane (n, h) holds dims 32mt + 8qd + 4h .. +3 of row n;
+        // 16-byte chunk c of row r sits at position c ^ (r % 8)) -> streaming
+        // 16-byte stores, 8 lanes per 128-byte line: stores of 8 bytes per
+        // lane, or streaming stores of partial lines, cost far more.
         const float inv = 1.0f / sum;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int d = 32 * mt + 8 * qd + 4 * h;
-                *reinterpret_cast<u32x2*>(tbuf + n * kKStride + d) =
-                    u32x2{pack2_bf16(oacc[mt][4 * qd + 0] * inv, oacc[mt][4 * qd + 1] * inv),
-                          pack2_bf16(oacc[mt][4 * qd + 2] * inv, oacc[mt][4 * qd + 3] * inv)};
-            }
-        __builtin_amdgcn_wave_barrier();
-        // partial-output row of bucket row rho = tile 32 + n: (base + rho / G)
-        // G + rho % G = base G + rho, so a tile's rows are consecutive (and
-        // stored with streaming stores); -1 for padding rows
         const int orow = cur_ok ? base * G + tile * 32 + n : -1;
+        uint16_t* sbuf = stg + wave * 32 * 64;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int r = lane / 16 + 4 * it;
-            const int o = __shfl(orow, r, kWave);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(tbuf + r * kKStride + 8 * (lane % 16));
-            uint16_t* dst = (o >= 0) ? w.part_o + (size_t)o * kHeadDim : w.trash_o;
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 8 * (lane % 16)));
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int mt = 2 * hf + m2;
+                    const int c = 4 * m2 + qd;
+                    *reinterpret_cast<u32x2*>(sbuf + n * 64 + 8 * (c ^ (n & 7)) + 4 * h) =
+                        u32x2{pack2_bf16(oacc[mt][4 * qd + 0] * inv, oacc[mt][4 * qd + 1] * inv),
+                              pack2_bf16(oacc[mt][4 * qd + 2] * inv, oacc[mt][4 * qd + 3] * inv)};
+                }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = lane / 8 + 8 * it;
+                const int c = lane % 8;
+                const int o = __shfl(orow, r, kWave);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sbuf + r * 64 + 8 * (c ^ (r & 7)));
+                uint16_t* dst = (o >= 0) ? w.part_o + (size_t)o * kHeadDim : w.trash_o;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 64 * hf + 8 * c));
+            }
+            __builtin_amdgcn_wave_barrier();
         }
         float* ldst = (cur_ok && h == 0) ? w.part_lse + orow : w.trash_lse + lane;
         *ldst = mx * scale_log2 * kLn2 + __logf(sum);
@@ -1256,9 +1278,9 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     const int n_bk = (int)std::min<int64_t>(NB, n_sel);
     const int n_large = (int)std::min<int64_t>(NB, n_sel / (small_cnt + 1));
     if (n_large > 0)
-        hipLaunchKernelGGL(block_major_kernel, dim3(n_large), dim3(kPfThreads), 0, st, q, k_cache, v_cache,
-                       block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
-                       s.scale * kLog2e);
+        hipLaunchKernelGGL(block_major_kernel, dim3(n_large), dim3(kPfThreads), 0, st, q, k_cache,
+                           v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
+                           s.scale * kLog2e);
     hipLaunchKernelGGL(bucket_small_kernel, dim3(n_bk), dim3(kDecThreads), 0, st, q, k_cache,
                        v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                        s.scale * kLog2e);
