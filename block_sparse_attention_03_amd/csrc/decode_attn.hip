@@ -383,30 +383,20 @@ void decode_multi_kernel(const float* __restrict__ scores,     // [B, Hkv, maxbl
 
 // Log-Sum-Exp merge of a row's pages: 16 threads per (row, head), each
 // merging 8 dims (one 16-byte piece of every page's bf16 partial); four
-// (row, head) pairs of one row per 64-thread workgroup.
+// (row, head) pairs per 64-thread workgroup.
 constexpr int kMergeThreads = 64;
 
 __global__ __launch_bounds__(kMergeThreads)
 void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __restrict__ ws,
                          uint16_t* __restrict__ out, float* __restrict__ lse_out, int Hq,
                          int Hkv, int R) {
-    // (row, item group) of this workgroup, the row placed as the page
-    // kernels place it (xcd_row): on the XCD whose L2 took the row's page
-    // partials (8 x 60k decode: 30.3 -> 29.9 us per step, same-box A/B)
+    const int idx = blockIdx.x * kMergeThreads + threadIdx.x;
     const int G = Hq / Hkv;
-    const int per_row = (G + kMergeThreads / 16 - 1) / (kMergeThreads / 16);
-    int x, r;
-    if (R % 8 == 0) {
-        const int lin = blockIdx.x;
-        x = (lin / 8) % per_row;
-        r = (lin / 8 / per_row) * 8 + lin % 8;
-    } else {
-        x = blockIdx.x % per_row;
-        r = blockIdx.x / per_row;
-    }
-    const int n = x * (kMergeThreads / 16) + threadIdx.x / 16;
-    const int part = threadIdx.x % 16;
-    if (r >= R || n >= G) return;
+    const int rn = idx / 16;  // r * G + n
+    const int part = idx % 16;
+    if (rn >= R * G) return;
+    const int r = rn / G;
+    const int n = rn % G;
     DecodeWs w = decode_ws(const_cast<void*>(ws), R, G);
     const float* lp = w.lse + (size_t)r * kTopK * G + n;
     // every slot's partial is loaded together with the row length (slots past
@@ -449,8 +439,8 @@ void decode_merge_kernel(const int32_t* __restrict__ row_lens, const void* __res
 hipError_t launch_merge(const MsaShape& s, const int32_t* row_lens, const void* ws, uint16_t* out,
                         float* lse, hipStream_t st) {
     const int R = s.B * s.Hkv;
-    const int per_row = ceil_div(s.Hq / s.Hkv, kMergeThreads / 16);
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(R * per_row), dim3(kMergeThreads),
+    const int n = R * (s.Hq / s.Hkv) * 16;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(ceil_div(n, kMergeThreads)), dim3(kMergeThreads),
                        0, st, row_lens, ws, out, lse, s.Hq, s.Hkv, R);
     return hipGetLastError();
 }
