@@ -519,8 +519,18 @@ void block_major_kernel(const uint16_t* __restrict__ q,        // [T, Hq, 128]
     __shared__ __attribute__((aligned(16))) uint16_t vs[kBlock * kHeadDim];
     __shared__ __attribute__((aligned(16))) uint16_t stg[(kPfThreads / kWave) * 32 * 64];
 
-    if ((int)blockIdx.x >= w.buckets[0]) return;  // uniform
-    const int bk = w.buckets[1 + blockIdx.x];
+    // Workgroups reach the 8 XCDs round-robin by index: XCD x takes list
+    // entries x per .. x per + per - 1, a contiguous run of the (sequence,
+    // group, block)-ordered list, so each XCD's L2 serves the query rows of
+    // about one eighth of the (sequence, group)s instead of all of them
+    // (8k chunk: attention call 0.948 -> 0.934 ms; with streaming query
+    // loads, which skip the caches, it takes 1.68 ms).  The grid is a
+    // multiple of 8 that covers every entry.
+    const int nbk = w.buckets[0];
+    const int per = (nbk + 7) / 8;
+    const int jj = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (jj >= nbk) return;  // uniform
+    const int bk = w.buckets[1 + jj];
     const int cnt = w.counts[bk];
     const int base = w.offsets[bk];
     const int b = bk % maxblk;
@@ -1278,8 +1288,8 @@ hipError_t msa_launch_prefill(const MsaShape& s, int total_q, const uint16_t* q,
     const int n_bk = (int)std::min<int64_t>(NB, n_sel);
     const int n_large = (int)std::min<int64_t>(NB, n_sel / (small_cnt + 1));
     if (n_large > 0)
-        hipLaunchKernelGGL(block_major_kernel, dim3(n_large), dim3(kPfThreads), 0, st, q, k_cache,
-                           v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
+        hipLaunchKernelGGL(block_major_kernel, dim3(ceil_div(n_large, 8) * 8), dim3(kPfThreads), 0,
+                           st, q, k_cache, v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
                            s.scale * kLog2e);
     hipLaunchKernelGGL(bucket_small_kernel, dim3(n_bk), dim3(kDecThreads), 0, st, q, k_cache,
                        v_cache, block_table, seq_lens, cu_q, w, s.Hq, s.Hkv, s.maxblk,
